@@ -1,0 +1,281 @@
+#!/usr/bin/env python3
+"""Throughput of exact tiled attention (forward + backward) on one MI355X.
+
+One step is the whole hot path over one batch of synthetic input: for each
+sub-workload, fa_fwd, then the three backward stages (fa_bwd_preprocess,
+fa_bwd_dkdv, fa_bwd_dq).  The default workload is long-context causal
+attention, B=1, H=16, N=16384, with both head dimensions d=64 and d=128 (the
+sequence length at which the forward target of half the bf16 MFMA peak is
+set).  HIP events recorded between consecutive launches on the launch stream
+give each kernel's average duration over the timed region.
+
+FLOP convention: 4*d per unmasked (query, key) pair for the forward and 10*d
+for the backward (its five products, including the recomputation of S);
+masked or skipped pairs are not counted.  Per kernel the algorithmic share is
+fwd 4d, dkdv 8d (S, dP, dV, dK), dq 2d (dQ only: its recomputation of S and dP
+is extra work and is not counted).
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0
+METRIC = "attention TFLOP/s fwd and fwd+bwd, % of MI355X bf16 MFMA peak, 1 GPU"
+
+BENCH_WORKLOADS = {
+    "long_causal_16k": ["long_d64", "long_d128"],
+    "long_d64": ["long_d64"],
+    "long_d128": ["long_d128"],
+    "bert_large": ["bert_large"],
+    "gpt2_small": ["gpt2_small"],
+    "blocksparse_64k": ["blocksparse_64k"],
+}
+
+KERNEL_SOURCES = ["fa_device.h", "fa_sched.h", "fa_fwd.h", "fa_bwd.h", "fa_api.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "exact_io_aware_18_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def pairs_per_head(N, causal, mask):
+    """Unmasked (query, key) pairs of one head."""
+    import torch
+
+    if mask is None:
+        return N * (N + 1) // 2 if causal else N * N
+    nb = mask.shape[0]
+    sizes = torch.full((nb,), 128, dtype=torch.int64)
+    sizes[-1] = N - 128 * (nb - 1)
+    m = (mask != 0).to(torch.int64)
+    total = int((sizes[:, None] * m * sizes[None, :]).sum())
+    if causal:
+        # diagonal blocks keep their lower triangle; blocks above it vanish
+        diag = int(((sizes * (sizes + 1)) // 2 * m.diagonal()).sum())
+        below = torch.tril(m, diagonal=-1)
+        total = diag + int((sizes[:, None] * below * sizes[None, :]).sum())
+    return total
+
+
+def load_traffic(kernel_key: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    ent = rec.get("kernels", {}).get(kernel_key)
+    return None if ent is None else ent.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(sub_names):
+    """The fp64 oracle, as it stands, on one head of each sub-workload (full
+    forward and backward), timed on this host's cores."""
+    import numpy as np
+
+    from exact_io_aware_18_amd.inputs import WORKLOADS, default_scale, make_blockmask, make_qkvdo
+    from oracle import attention_bwd, attention_fwd
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    flops = 0.0
+    secs = 0.0
+    desc = []
+    for name in sub_names:
+        w = WORKLOADS[name]
+        N, d = w["N"], w["d"]
+        q, k, v, do = make_qkvdo(1, 1, N, d, w["dtype"], seed=0)
+        mask = make_blockmask(N, w.get("frac", 0.125)) if w["mask"] else None
+        m = None if mask is None else mask.numpy()
+        q64, k64, v64, do64 = (t.double().numpy() for t in (q, k, v, do))
+        t0 = time.perf_counter()
+        attention_fwd(q64, k64, v64, default_scale(d), w["causal"], m)
+        attention_bwd(q64, k64, v64, do64, default_scale(d), w["causal"], m)
+        secs += time.perf_counter() - t0
+        flops += 14.0 * d * pairs_per_head(N, w["causal"], mask)
+        desc.append(f"{name}: B=1 H=1 N={N} d={d}")
+    return {
+        "value": flops / secs / 1e12,
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": "full fp64 forward+backward of one head of each sub-workload (" + "; ".join(desc)
+                  + f"), {secs:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long_causal_16k", choices=sorted(BENCH_WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: every (batch, head) is independent, so the kernel "
+              "is benchmarked on one GPU's share; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exact_io_aware_18_amd as fa
+    from exact_io_aware_18_amd.inputs import WORKLOADS, default_scale, make_blockmask, make_qkvdo
+
+    fa.lib()
+    dev = torch.device("cuda:0")
+    subs = []
+    for name in BENCH_WORKLOADS[args.workload]:
+        w = WORKLOADS[name]
+        B, H, N, d = w["B"], w["H"], w["N"], w["d"]
+        q, k, v, do = (t.to(dev) for t in make_qkvdo(B, H, N, d, "bf16", seed=0))
+        mask = make_blockmask(N, w.get("frac", 0.125)) if w["mask"] else None
+        pairs = B * H * pairs_per_head(N, w["causal"], mask)
+        sub = dict(name=name, B=B, H=H, N=N, d=d, causal=w["causal"], pairs=pairs,
+                   q=q, k=k, v=v, do=do, mask=None if mask is None else mask.to(dev),
+                   scale=default_scale(d))
+        sub["o"] = torch.empty_like(q)
+        sub["lse"] = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        sub["grads"] = tuple(torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(3))
+        sub["ws"] = torch.empty(fa.fa_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+        subs.append(sub)
+
+    stream = torch.cuda.current_stream()
+    nk = 4  # kernels per sub-workload per step
+
+    def step(events=None):
+        for si, s in enumerate(subs):
+            base = si * nk
+            if events is not None:
+                events[base].record(stream)
+            fa.fwd(s["q"], s["k"], s["v"], s["scale"], s["causal"], s["mask"], out=s["o"], lse=s["lse"])
+            B, H, N, d = s["B"], s["H"], s["N"], s["d"]
+            wsp, wsn = s["ws"].data_ptr(), s["ws"].numel()
+            sp = stream.cuda_stream
+            dq, dk, dv = s["grads"]
+            mp = None if s["mask"] is None else s["mask"].data_ptr()
+            if events is not None:
+                events[base + 1].record(stream)
+            fa._check(fa.fa_bwd_preprocess(s["o"].data_ptr(), s["do"].data_ptr(), B, H, N, d, wsp,
+                                           wsn, sp), "fa_bwd_preprocess")
+            if events is not None:
+                events[base + 2].record(stream)
+            fa._check(fa.fa_bwd_dkdv(s["q"].data_ptr(), s["k"].data_ptr(), s["v"].data_ptr(),
+                                     s["lse"].data_ptr(), s["do"].data_ptr(), dk.data_ptr(),
+                                     dv.data_ptr(), B, H, N, d, s["scale"], int(s["causal"]), mp,
+                                     wsp, wsn, sp), "fa_bwd_dkdv")
+            if events is not None:
+                events[base + 3].record(stream)
+            fa._check(fa.fa_bwd_dq(s["q"].data_ptr(), s["k"].data_ptr(), s["v"].data_ptr(),
+                                   s["lse"].data_ptr(), s["do"].data_ptr(), dq.data_ptr(), B, H, N,
+                                   d, s["scale"], int(s["causal"]), mp, wsp, wsn, sp), "fa_bwd_dq")
+        if events is not None:
+            events[len(subs) * nk].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    nev = len(subs) * nk + 1
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    kinds = ["fwd", "bwd_pre", "bwd_dkdv", "bwd_dq"]
+    kernels = {}
+    for si, s in enumerate(subs):
+        for j, kind in enumerate(kinds):
+            a = si * nk + j
+            ms = sum(evs[i][a].elapsed_time(evs[i][a + 1]) for i in range(args.steps)) / args.steps
+            key = f"{kind}_d{s['d']}"
+            kernels[key] = {"ms": ms}
+            d, p, rows = s["d"], s["pairs"], s["B"] * s["H"] * s["N"]
+            if kind == "fwd":
+                kernels[key]["flops"] = 4.0 * d * p
+            elif kind == "bwd_dkdv":
+                kernels[key]["flops"] = 8.0 * d * p
+            elif kind == "bwd_dq":
+                kernels[key]["flops"] = 2.0 * d * p
+            else:
+                kernels[key]["bytes"] = rows * (2 * d * 2 + 4)
+            if "flops" in kernels[key]:
+                kernels[key]["tflops"] = kernels[key]["flops"] / (ms * 1e-3) / 1e12
+            else:
+                kernels[key]["gbs"] = kernels[key]["bytes"] / (ms * 1e-3) / 1e9
+
+    fwd_flops = sum(4.0 * s["d"] * s["pairs"] for s in subs)
+    bwd_flops = sum(10.0 * s["d"] * s["pairs"] for s in subs)
+    fwd_ms = sum(kernels[f"fwd_d{s['d']}"]["ms"] for s in subs)
+    value = (fwd_flops + bwd_flops) / (ms_per_step * 1e-3) / 1e12
+
+    dom = max(kernels, key=lambda k_: kernels[k_]["ms"])
+    dk_ = kernels[dom]
+    if "flops" in dk_:
+        achieved, peak, unit, bound = dk_["tflops"], PEAK_BF16_TFLOPS, "TFLOP/s", "mfma"
+    else:
+        achieved, peak, unit, bound = dk_["gbs"], PEAK_HBM_GBS, "GB/s", "hbm"
+    roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": load_traffic(dom), "kernel": dom,
+                "kernel_ms": round(dk_["ms"], 4)}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload,
+            "subs": [f"{s['name']}: B={s['B']} H={s['H']} N={s['N']} d={s['d']} "
+                     f"causal={int(s['causal'])} mask={int(s['mask'] is not None)}" for s in subs],
+            "parallelism": "single GPU",
+        },
+        "fwd_tflops": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 2),
+        "fwd_frac_peak": round(fwd_flops / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "fwd_bwd_frac_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "kernels": {k_: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v_.items()}
+                    for k_, v_ in kernels.items()},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline([s["name"] for s in subs])
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,410 @@
+// C ABI of the attention library: argument checks, variant dispatch and
+// launches.  Every check runs before the first HIP call, so an invalid call
+// enqueues nothing and is testable without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/fa.h"
+#include "fa_bwd.h"
+#include "fa_f32.h"
+#include "fa_fwd.h"
+
+namespace {
+
+constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+
+struct Span {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Span span(const void* p, size_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Span{a, a + bytes};
+}
+
+bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned(const void* p, size_t al) { return (reinterpret_cast<uintptr_t>(p) % al) == 0; }
+
+int nblocks(int N) { return (N + 127) / 128; }
+
+// Shape limits shared by every call.
+int check_shape(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if ((long long)N * d >= (1LL << 31)) return FA_ERR_SHAPE;
+  const long long bh = (long long)B * H;
+  if (bh * nblocks(N) >= (1LL << 24)) return FA_ERR_SHAPE;
+  if (bh * N * d >= (1LL << 46)) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+int check_flags(float scale, int causal) {
+  if (causal != 0 && causal != 1) return FA_ERR_FLAG;
+  if (!std::isfinite(scale)) return FA_ERR_SCALE;
+  return FA_OK;
+}
+
+// Outputs must not overlap inputs or each other.
+int check_alias(const Span* outs, int nout, const Span* ins, int nin) {
+  for (int i = 0; i < nout; ++i) {
+    for (int j = 0; j < nin; ++j)
+      if (overlap(outs[i], ins[j])) return FA_ERR_ALIAS;
+    for (int j = i + 1; j < nout; ++j)
+      if (overlap(outs[i], outs[j])) return FA_ERR_ALIAS;
+  }
+  return FA_OK;
+}
+
+size_t workspace_bytes(int B, int H, int N) {
+  const size_t n = (size_t)B * H * N * sizeof(float);
+  return (n + 255) & ~(size_t)255;
+}
+
+int launched() {
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+// ---- bf16 forward -----------------------------------------------------------
+template <int D, bool CAUSAL, bool MASK>
+void launch_fwd_t(const fa::FwdArgs& a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((fa::fwd_bf16_kernel<D, CAUSAL, MASK>), dim3(grid), dim3(256), 0, s, a);
+}
+
+template <int D>
+void launch_fwd_d(const fa::FwdArgs& a, int grid, bool causal, bool mask, hipStream_t s) {
+  if (causal) {
+    if (mask) launch_fwd_t<D, true, true>(a, grid, s);
+    else launch_fwd_t<D, true, false>(a, grid, s);
+  } else {
+    if (mask) launch_fwd_t<D, false, true>(a, grid, s);
+    else launch_fwd_t<D, false, false>(a, grid, s);
+  }
+}
+
+// ---- bf16 backward ----------------------------------------------------------
+enum BwdStage { kPre = 1, kDkdv = 2, kDq = 4 };
+
+template <int D, bool CAUSAL, bool MASK>
+void launch_bwd_t(fa::BwdArgs a, int BH, int stages, hipStream_t s) {
+  a.total = BH * a.ntile;
+  if (stages & kDkdv)
+    hipLaunchKernelGGL((fa::bwd_dkdv_kernel<D, CAUSAL, MASK>), dim3(a.total), dim3(256), 0, s, a);
+  if (stages & kDq)
+    hipLaunchKernelGGL((fa::bwd_dq_kernel<D, CAUSAL, MASK>), dim3(a.total), dim3(256), 0, s, a);
+}
+
+template <int D>
+void launch_bwd_d(const fa::BwdArgs& a, int BH, bool causal, bool mask, int stages, hipStream_t s) {
+  if (stages & kPre) {
+    const long rows = (long)BH * a.N;
+    const int pre_grid = (int)((rows * (D / 8) + 255) / 256);
+    hipLaunchKernelGGL((fa::bwd_pre_kernel<D>), dim3(pre_grid), dim3(256), 0, s, a.o, a.dout, a.Dw, rows);
+  }
+  if (causal) {
+    if (mask) launch_bwd_t<D, true, true>(a, BH, stages, s);
+    else launch_bwd_t<D, true, false>(a, BH, stages, s);
+  } else {
+    if (mask) launch_bwd_t<D, false, true>(a, BH, stages, s);
+    else launch_bwd_t<D, false, false>(a, BH, stages, s);
+  }
+}
+
+int run_bwd(const fa::BwdArgs& a, int BH, int d, int causal, bool mask, int stages, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (d == 64) launch_bwd_d<64>(a, BH, causal, mask, stages, s);
+  else launch_bwd_d<128>(a, BH, causal, mask, stages, s);
+  return launched();
+}
+
+// ---- fp32 -------------------------------------------------------------------
+template <int D>
+void launch_fwd_f32_d(const fa::F32Args& a, int BH, hipStream_t s) {
+  dim3 grid((a.N + fa::kF32Rows - 1) / fa::kF32Rows, BH);
+  hipLaunchKernelGGL((fa::fwd_f32_kernel<D>), grid, dim3(256), 0, s, a);
+}
+
+template <int D>
+void launch_bwd_f32_d(fa::F32Args a, int BH, float* dq, float* dk, float* dv, hipStream_t s) {
+  const long rows = (long)BH * a.N;
+  hipLaunchKernelGGL((fa::bwd_pre_f32_kernel<D>), dim3((unsigned)((rows + 63) / 64)), dim3(256), 0, s, a, rows);
+  dim3 grid((a.N + fa::kF32Rows - 1) / fa::kF32Rows, BH);
+  a.dst0 = dq;
+  hipLaunchKernelGGL((fa::bwd_dq_f32_kernel<D>), grid, dim3(256), 0, s, a);
+  a.dst0 = dk;
+  a.dst1 = dv;
+  hipLaunchKernelGGL((fa::bwd_dkdv_f32_kernel<D>), grid, dim3(256), 0, s, a);
+}
+
+// A tensor argument: address, extent in bytes, required alignment.
+struct Buf {
+  const void* p;
+  size_t bytes;
+  size_t align;
+};
+
+// Null, alignment and overlap checks over the inputs and outputs of a call.
+// `ins` may hold entries with p == nullptr that are optional (the mask).
+int check_bufs(const Buf* ins, int nin, const Buf* outs, int nout) {
+  for (int i = 0; i < nout; ++i)
+    if (!outs[i].p) return FA_ERR_NULL;
+  for (int i = 0; i < nin; ++i)
+    if (ins[i].p && !aligned(ins[i].p, ins[i].align)) return FA_ERR_ALIGN;
+  for (int i = 0; i < nout; ++i)
+    if (!aligned(outs[i].p, outs[i].align)) return FA_ERR_ALIGN;
+  Span si[8], so[8];
+  int ni = 0;
+  for (int i = 0; i < nin; ++i)
+    if (ins[i].p) si[ni++] = span(ins[i].p, ins[i].bytes);
+  for (int i = 0; i < nout; ++i) so[i] = span(outs[i].p, outs[i].bytes);
+  return check_alias(so, nout, si, ni);
+}
+
+struct Sizes {
+  size_t t;   // one [B,H,N,d] input tensor
+  size_t g;   // one fp32 [B,H,N,d] gradient
+  size_t l;   // one fp32 [B,H,N] vector
+  size_t m;   // block mask
+  size_t ws;  // workspace
+};
+
+Sizes sizes(int B, int H, int N, int d, size_t esz) {
+  const size_t rows = (size_t)B * H * N;
+  const size_t nb = (size_t)nblocks(N);
+  return Sizes{rows * d * esz, rows * d * sizeof(float), rows * sizeof(float), nb * nb,
+               workspace_bytes(B, H, N)};
+}
+
+int check_common(int B, int H, int N, int d, float scale, int causal) {
+  int st = check_shape(B, H, N, d);
+  if (st) return st;
+  return check_flags(scale, causal);
+}
+
+int check_fwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+              int B, int H, int N, int d, float scale, int causal, const unsigned char* mask,
+              size_t esz) {
+  if (!q || !k || !v) return FA_ERR_NULL;
+  int st = check_common(B, H, N, d, scale, causal);
+  if (st) return st;
+  const Sizes z = sizes(B, H, N, d, esz);
+  const Buf ins[4] = {{q, z.t, 16}, {k, z.t, 16}, {v, z.t, 16}, {mask, z.m, 1}};
+  const Buf outs[2] = {{o, z.t, 16}, {lse, z.l, 4}};
+  return check_bufs(ins, 4, outs, 2);
+}
+
+int check_ws(const void* ws, size_t ws_bytes, int B, int H, int N) {
+  if (!ws || ws_bytes < workspace_bytes(B, H, N)) return FA_ERR_WORKSPACE;
+  if (!aligned(ws, 16)) return FA_ERR_ALIGN;
+  return FA_OK;
+}
+
+int check_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+              const void* dout, const float* dq, const float* dk, const float* dv, int B, int H,
+              int N, int d, float scale, int causal, const unsigned char* mask,
+              const void* ws, size_t ws_bytes, size_t esz) {
+  if (!q || !k || !v || !o || !lse || !dout) return FA_ERR_NULL;
+  int st = check_common(B, H, N, d, scale, causal);
+  if (st) return st;
+  if ((st = check_ws(ws, ws_bytes, B, H, N))) return st;
+  const Sizes z = sizes(B, H, N, d, esz);
+  const Buf ins[7] = {{q, z.t, 16}, {k, z.t, 16}, {v, z.t, 16}, {o, z.t, 16},
+                      {dout, z.t, 16}, {lse, z.l, 4}, {mask, z.m, 1}};
+  const Buf outs[4] = {{dq, z.g, 16}, {dk, z.g, 16}, {dv, z.g, 16}, {ws, z.ws, 16}};
+  return check_bufs(ins, 7, outs, 4);
+}
+
+fa::BwdArgs bwd_args(const void* q, const void* k, const void* v, const void* o,
+                     const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                     int N, float scale, const unsigned char* mask, void* ws) {
+  fa::BwdArgs a;
+  a.q = static_cast<const __bf16*>(q);
+  a.k = static_cast<const __bf16*>(k);
+  a.v = static_cast<const __bf16*>(v);
+  a.o = static_cast<const __bf16*>(o);
+  a.dout = static_cast<const __bf16*>(dout);
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.Dw = static_cast<float*>(ws);
+  a.mask = mask;
+  a.N = N;
+  a.nb = nblocks(N);
+  a.ntile = (N + 127) / 128;  // dK/dV and dQ workgroups each own 128 rows
+  a.total = 0;
+  a.c = scale * fa::kLog2e;
+  a.scale = scale;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+           int d, float scale, int causal, const unsigned char* blockmask, void* stream) {
+  int st = check_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, blockmask, 2);
+  if (st) return st;
+  fa::FwdArgs a;
+  a.q = static_cast<const __bf16*>(q);
+  a.k = static_cast<const __bf16*>(k);
+  a.v = static_cast<const __bf16*>(v);
+  a.o = static_cast<__bf16*>(o);
+  a.lse = lse;
+  a.mask = blockmask;
+  a.N = N;
+  a.nqt = (N + 127) / 128;
+  a.total = B * H * a.nqt;
+  a.nb = nblocks(N);
+  a.c = std::fabs(scale) * fa::kLog2e;
+  a.negate_q = scale < 0.f;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (d == 64) launch_fwd_d<64>(a, a.total, causal, blockmask != nullptr, s);
+  else launch_fwd_d<128>(a, a.total, causal, blockmask != nullptr, s);
+  return launched();
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, float* dq, float* dk, float* dv, int B, int H, int N, int d,
+           float scale, int causal, const unsigned char* blockmask, void* workspace,
+           size_t workspace_bytes_, void* stream) {
+  int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, blockmask,
+                     workspace, workspace_bytes_, 2);
+  if (st) return st;
+  const fa::BwdArgs a = bwd_args(q, k, v, o, lse, dout, dq, dk, dv, N, scale, blockmask, workspace);
+  return run_bwd(a, B * H, d, causal, blockmask != nullptr, kPre | kDkdv | kDq, stream);
+}
+
+int fa_bwd_preprocess(const void* o, const void* dout, int B, int H, int N, int d,
+                      void* workspace, size_t workspace_bytes_, void* stream) {
+  if (!o || !dout) return FA_ERR_NULL;
+  int st = check_shape(B, H, N, d);
+  if (st) return st;
+  if ((st = check_ws(workspace, workspace_bytes_, B, H, N))) return st;
+  const Sizes z = sizes(B, H, N, d, 2);
+  const Buf ins[2] = {{o, z.t, 16}, {dout, z.t, 16}};
+  const Buf outs[1] = {{workspace, z.ws, 16}};
+  if ((st = check_bufs(ins, 2, outs, 1))) return st;
+  const fa::BwdArgs a = bwd_args(nullptr, nullptr, nullptr, o, nullptr, dout, nullptr, nullptr,
+                                 nullptr, N, 1.f, nullptr, workspace);
+  return run_bwd(a, B * H, d, 0, false, kPre, stream);
+}
+
+int fa_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dout,
+                float* dk, float* dv, int B, int H, int N, int d, float scale, int causal,
+                const unsigned char* blockmask, const void* workspace, size_t workspace_bytes_,
+                void* stream) {
+  if (!q || !k || !v || !lse || !dout) return FA_ERR_NULL;
+  int st = check_common(B, H, N, d, scale, causal);
+  if (st) return st;
+  if ((st = check_ws(workspace, workspace_bytes_, B, H, N))) return st;
+  const Sizes z = sizes(B, H, N, d, 2);
+  const Buf ins[7] = {{q, z.t, 16}, {k, z.t, 16}, {v, z.t, 16}, {dout, z.t, 16},
+                      {lse, z.l, 4}, {workspace, z.ws, 16}, {blockmask, z.m, 1}};
+  const Buf outs[2] = {{dk, z.g, 16}, {dv, z.g, 16}};
+  if ((st = check_bufs(ins, 7, outs, 2))) return st;
+  const fa::BwdArgs a = bwd_args(q, k, v, nullptr, lse, dout, nullptr, dk, dv, N, scale, blockmask,
+                                 const_cast<void*>(workspace));
+  return run_bwd(a, B * H, d, causal, blockmask != nullptr, kDkdv, stream);
+}
+
+int fa_bwd_dq(const void* q, const void* k, const void* v, const float* lse, const void* dout,
+              float* dq, int B, int H, int N, int d, float scale, int causal,
+              const unsigned char* blockmask, const void* workspace, size_t workspace_bytes_,
+              void* stream) {
+  if (!q || !k || !v || !lse || !dout) return FA_ERR_NULL;
+  int st = check_common(B, H, N, d, scale, causal);
+  if (st) return st;
+  if ((st = check_ws(workspace, workspace_bytes_, B, H, N))) return st;
+  const Sizes z = sizes(B, H, N, d, 2);
+  const Buf ins[7] = {{q, z.t, 16}, {k, z.t, 16}, {v, z.t, 16}, {dout, z.t, 16},
+                      {lse, z.l, 4}, {workspace, z.ws, 16}, {blockmask, z.m, 1}};
+  const Buf outs[1] = {{dq, z.g, 16}};
+  if ((st = check_bufs(ins, 7, outs, 1))) return st;
+  const fa::BwdArgs a = bwd_args(q, k, v, nullptr, lse, dout, dq, nullptr, nullptr, N, scale,
+                                 blockmask, const_cast<void*>(workspace));
+  return run_bwd(a, B * H, d, causal, blockmask != nullptr, kDq, stream);
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
+  if (check_shape(B, H, N, d) != FA_OK) return 0;
+  return workspace_bytes(B, H, N);
+}
+
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,
+               int N, int d, float scale, int causal, const unsigned char* blockmask,
+               void* stream) {
+  int st = check_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, blockmask, 4);
+  if (st) return st;
+  if ((long long)B * H >= 65536) return FA_ERR_UNSUPPORTED;  // grid.y limit
+  fa::F32Args a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dst0 = o;
+  a.out_lse = lse;
+  a.mask = blockmask;
+  a.N = N;
+  a.nb = nblocks(N);
+  a.causal = causal;
+  a.scale = scale;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (d == 64) launch_fwd_f32_d<64>(a, B * H, s);
+  else launch_fwd_f32_d<128>(a, B * H, s);
+  return launched();
+}
+
+int fa_bwd_f32(const float* q, const float* k, const float* v, const float* o, const float* lse,
+               const float* dout, float* dq, float* dk, float* dv, int B, int H, int N, int d,
+               float scale, int causal, const unsigned char* blockmask, void* workspace,
+               size_t workspace_bytes_, void* stream) {
+  int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, blockmask,
+                     workspace, workspace_bytes_, 4);
+  if (st) return st;
+  if ((long long)B * H >= 65536) return FA_ERR_UNSUPPORTED;
+  fa::F32Args a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.dout = dout;
+  a.Dw = static_cast<float*>(workspace);
+  a.mask = blockmask;
+  a.N = N;
+  a.nb = nblocks(N);
+  a.causal = causal;
+  a.scale = scale;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (d == 64) launch_bwd_f32_d<64>(a, B * H, dq, dk, dv, s);
+  else launch_bwd_f32_d<128>(a, B * H, dq, dk, dv, s);
+  return launched();
+}
+
+const char* fa_strerror(int status) {
+  switch (status) {
+    case FA_OK: return "success";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "B, H or N is below 1 or a size limit is exceeded";
+    case FA_ERR_HEADDIM: return "head dimension d must be 64 or 128";
+    case FA_ERR_ALIGN: return "tensor pointers must be 16-byte aligned (lse 4-byte)";
+    case FA_ERR_ALIAS: return "an output overlaps an input or another output";
+    case FA_ERR_WORKSPACE: return "workspace is NULL or smaller than fa_bwd_workspace_bytes()";
+    case FA_ERR_FLAG: return "causal must be 0 or 1";
+    case FA_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
+    case FA_ERR_UNSUPPORTED: return "arguments are valid but not supported by this build";
+    case FA_ERR_SCALE: return "scale must be finite";
+    default: return "unknown status";
+  }
+}
+
+int fa_version(void) { return kVersion; }
+
+}  // extern "C"

@@ -1,0 +1,137 @@
+/*
+ * fa.h - C ABI of an exact, tile-by-tile attention library for MI355X (gfx950).
+ *
+ * What the calls compute.  Standard scaled-dot-product attention per
+ * (batch, head): S = scale * Q K^T, P = softmax(S) row-wise, O = P V
+ * ("FlashAttention: Fast and Memory-Efficient Exact Attention with
+ * IO-Awareness", summary page, §2 Background), computed without ever writing
+ * S or P to HBM: Q/K/V are split into tiles staged on-chip, the softmax is
+ * normalised incrementally across key tiles, and only O plus one per-row
+ * statistic (the logsumexp) go back to memory (same page, §3 Method:
+ * "Tiling" and "Softmax rescaling / recomputation").  The backward pass
+ * recomputes P on-chip from that statistic (same section) and returns the
+ * exact gradients of O with respect to Q, K and V.  Block-sparse attention
+ * skips the key blocks a block mask zeroes (abstract on the same pages:
+ * "We also extend FlashAttention to block-sparse attention").
+ *
+ * Conventions shared by every call
+ *   - Tensors are [B, H, N, d], contiguous, d fastest.  Q, K and V have the
+ *     same N (self-attention shape).  lse and the backward workspace are
+ *     [B, H, N] fp32.
+ *   - lse[b,h,i] = ln sum_j exp(S_ij) over allowed j (natural log of the
+ *     scaled scores).  A row with no allowed key gets O = 0 and lse = -inf,
+ *     and contributes nothing to the gradients.
+ *   - causal != 0 keeps key j for query i only when j <= i.
+ *   - blockmask: NULL for dense, else a device array of nb*nb bytes with
+ *     nb = ceil(N/128); entry [qb*nb + kb] != 0 lets query rows of block qb
+ *     see key rows of block kb.  One mask serves every (b, h).  The last
+ *     block covers the remainder when N % 128 != 0.  causal and blockmask
+ *     combine by AND.
+ *   - Ownership: every pointer is caller-owned device memory.  The library
+ *     allocates nothing, frees nothing and keeps no state, so concurrent
+ *     calls on different streams are safe.  Inputs are only read; outputs
+ *     are fully overwritten.
+ *   - Asynchrony: work is enqueued on `stream` (a hipStream_t, NULL = the
+ *     null stream) and the call returns without waiting.
+ *   - Errors: arguments are checked before any HIP call, so a bad call
+ *     returns a negative fa_status and enqueues nothing.  A failed launch
+ *     returns FA_ERR_LAUNCH.  Faults inside a kernel surface at the caller's
+ *     next synchronisation.  No C++ exception crosses this interface.
+ *   - Supported: d in {64, 128}; B, H, N >= 1; N * d < 2^31;
+ *     B * H * ceil(N/128) < 2^24; scale finite.
+ *     Tensor pointers must be 16-byte aligned, lse 4-byte aligned.
+ *     No output may overlap an input or another output.
+ */
+#ifndef FA_MI355X_FA_H
+#define FA_MI355X_FA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_NULL = -1,        /* a required pointer is NULL */
+    FA_ERR_SHAPE = -2,       /* B, H or N < 1, or a size limit exceeded */
+    FA_ERR_HEADDIM = -3,     /* d is not 64 or 128 */
+    FA_ERR_ALIGN = -4,       /* a pointer is not aligned as required */
+    FA_ERR_ALIAS = -5,       /* an output overlaps an input or another output */
+    FA_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than fa_bwd_workspace_bytes() */
+    FA_ERR_FLAG = -7,        /* causal is not 0 or 1 */
+    FA_ERR_LAUNCH = -8,      /* the HIP runtime rejected a kernel launch */
+    FA_ERR_UNSUPPORTED = -9, /* valid arguments this build does not handle */
+    FA_ERR_SCALE = -10       /* scale is NaN or infinite */
+} fa_status;
+
+/*
+ * Forward, bf16.  q, k, v: bf16 [B,H,N,d] (uint16 storage).  o: bf16
+ * [B,H,N,d], rounded to nearest even from the fp32 accumulator.  lse: fp32
+ * [B,H,N].  Computes O = softmax(scale * Q K^T, masked) V row by row with an
+ * online softmax over key tiles (§3 Method, "Tiling", "Softmax rescaling").
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, float scale, int causal,
+           const unsigned char* blockmask, void* stream);
+
+/*
+ * Backward, bf16 inputs, fp32 gradients.  q, k, v, o, dout: bf16 [B,H,N,d];
+ * o and lse must be the outputs of fa_fwd on the same q, k, v, scale, causal
+ * and blockmask.  dq, dk, dv: fp32 [B,H,N,d], fully overwritten.  P is
+ * recomputed from lse instead of being read from memory (§3 Method,
+ * "recomputation").  workspace: device memory of at least
+ * fa_bwd_workspace_bytes(B,H,N,d) bytes, 16-byte aligned; its contents on
+ * entry are ignored and on exit are unspecified.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+           const float* lse, const void* dout, float* dq, float* dk, float* dv,
+           int B, int H, int N, int d, float scale, int causal,
+           const unsigned char* blockmask, void* workspace,
+           size_t workspace_bytes, void* stream);
+
+/*
+ * The three stages fa_bwd runs, in this order, as separate calls (bf16 path)
+ * for callers that schedule or time them one by one.  Arguments mean what
+ * they mean for fa_bwd; each call checks only the arguments it uses.
+ *   fa_bwd_preprocess  D_i = sum_c dout_ic * o_ic into the workspace
+ *   fa_bwd_dkdv        dk and dv (needs the preprocess result)
+ *   fa_bwd_dq          dq (needs the preprocess result)
+ */
+int fa_bwd_preprocess(const void* o, const void* dout, int B, int H, int N, int d,
+                      void* workspace, size_t workspace_bytes, void* stream);
+int fa_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
+                const void* dout, float* dk, float* dv, int B, int H, int N, int d,
+                float scale, int causal, const unsigned char* blockmask,
+                const void* workspace, size_t workspace_bytes, void* stream);
+int fa_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
+              const void* dout, float* dq, int B, int H, int N, int d, float scale,
+              int causal, const unsigned char* blockmask, const void* workspace,
+              size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace fa_bwd and fa_bwd_f32 need (0 for invalid sizes). */
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
+
+/* Forward with fp32 tensors throughout (fp32 arithmetic, fp32 O and lse). */
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o,
+               float* lse, int B, int H, int N, int d, float scale,
+               int causal, const unsigned char* blockmask, void* stream);
+
+/* Backward with fp32 tensors throughout.  Arguments as for fa_bwd. */
+int fa_bwd_f32(const float* q, const float* k, const float* v,
+               const float* o, const float* lse, const float* dout,
+               float* dq, float* dk, float* dv, int B, int H, int N, int d,
+               float scale, int causal, const unsigned char* blockmask,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static English text for a status code (never NULL). */
+const char* fa_strerror(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_FA_H */

@@ -1,0 +1,200 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 CPU oracle.
+
+Tolerances (max-abs per tensor, any NaN fails): O, dQ, dK, dV <= 2e-2 for
+bf16 inputs and <= 1e-5 on the fp32 path; lse <= 1e-3.
+"""
+import numpy as np
+import pytest
+import torch
+
+from exact_io_aware_18_amd.inputs import (
+    WORKLOADS,
+    default_scale,
+    make_blockmask,
+    make_qkvdo,
+    make_random_blockmask,
+    sample_rows,
+    workload_inputs,
+)
+from oracle import (
+    attention_bwd,
+    attention_dkdv_rows,
+    attention_dq_rows,
+    attention_fwd,
+    attention_fwd_rows,
+)
+from tests.gpu_helpers import check, device, run_gpu, to64
+
+pytestmark = pytest.mark.gpu
+
+
+def full_parity(q, k, v, do, scale, causal, mask, dtype, backward=True):
+    dev = device()
+    print(f"\n[parity] shape={tuple(q.shape)} dtype={dtype} causal={causal} "
+          f"mask={mask is not None} scale={scale:.4f}", flush=True)
+    got = run_gpu(q, k, v, do, scale, causal, mask, dtype, dev, backward)
+    q64, k64, v64, do64 = (to64(t) for t in (q, k, v, do))
+    m = None if mask is None else mask.numpy()
+    o_ref, lse_ref = attention_fwd(q64, k64, v64, scale, causal, m)
+    rep = {}
+    check("o", to64(got["o"]), o_ref, dtype, rep)
+    check("lse", to64(got["lse"]), lse_ref, dtype, rep)
+    if backward:
+        dq, dk, dv = attention_bwd(q64, k64, v64, do64, scale, causal, m)
+        check("dq", to64(got["dq"]), dq, dtype, rep)
+        check("dk", to64(got["dk"]), dk, dtype, rep)
+        check("dv", to64(got["dv"]), dv, dtype, rep)
+    print("[parity] max-abs:", {k_: f"{v_:.2e}" for k_, v_ in rep.items()}, flush=True)
+    return got
+
+
+# ---- the named workloads ------------------------------------------------------
+def test_tiny_f32_forward_and_backward():
+    q, k, v, do, scale, causal, mask = workload_inputs("tiny_f32")
+    full_parity(q, k, v, do, scale, causal, mask, "f32")
+
+
+@pytest.mark.parametrize("name", ["bert_large", "gpt2_small"])
+def test_full_workloads(name):
+    q, k, v, do, scale, causal, mask = workload_inputs(name)
+    full_parity(q, k, v, do, scale, causal, mask, "bf16")
+
+
+@pytest.mark.parametrize("name", ["long_d64", "long_d128", "blocksparse_64k"])
+def test_large_workloads_sampled(name):
+    """Full-size launch; O, lse and dQ checked at 256 seeded query rows, dK and
+    dV at the sampled positions of two heads taken as key rows, plus
+    invariants over every row."""
+    dev = device()
+    w = WORKLOADS[name]
+    q, k, v, do, scale, causal, mask = workload_inputs(name)
+    print(f"\n[sampled] {name} shape={tuple(q.shape)} causal={causal} mask={mask is not None}", flush=True)
+    got = run_gpu(q, k, v, do, scale, causal, mask, "bf16", dev)
+    b, h, i = (x.numpy() for x in sample_rows(w["B"], w["H"], w["N"]))
+    q64, k64, v64, do64 = (to64(t) for t in (q, k, v, do))
+    m = None if mask is None else mask.numpy()
+    rep = {}
+    o_ref, lse_ref = attention_fwd_rows(q64, k64, v64, scale, causal, m, b, h, i)
+    check("o", to64(got["o"])[b, h, i], o_ref, "bf16", rep)
+    check("lse", to64(got["lse"])[b, h, i], lse_ref, "bf16", rep)
+    dq_ref = attention_dq_rows(q64, k64, v64, do64, scale, causal, m, b, h, i)
+    check("dq", to64(got["dq"])[b, h, i], dq_ref, "bf16", rep)
+    heads = sorted(set(h.tolist()))[:2]
+    sel = np.isin(h, heads)
+    dk_ref, dv_ref = attention_dkdv_rows(q64, k64, v64, do64, scale, causal, m, b[sel], h[sel], i[sel])
+    check("dk", to64(got["dk"])[b[sel], h[sel], i[sel]], dk_ref, "bf16", rep)
+    check("dv", to64(got["dv"])[b[sel], h[sel], i[sel]], dv_ref, "bf16", rep)
+    print(f"[sampled] {name} max-abs ({sel.sum()} key rows):", {k_: f"{v_:.2e}" for k_, v_ in rep.items()}, flush=True)
+    # invariants over all rows (exact in real arithmetic for any mask)
+    dkf, dvf, dqf = to64(got["dk"]), to64(got["dv"]), to64(got["dq"])
+    N = w["N"]
+    tol_sum = 2e-2 * np.sqrt(N)
+    assert np.abs(dkf.sum(axis=2)).max() <= tol_sum
+    assert np.abs(dvf.sum(axis=2) - do64.sum(axis=2)).max() <= tol_sum
+    lhs = (q64 * dqf).sum(axis=(2, 3))
+    rhs = (k64 * dkf).sum(axis=(2, 3))
+    assert np.abs(lhs - rhs).max() <= 2e-2 * N
+
+
+# ---- edge shapes ----------------------------------------------------------------
+EDGE_N = [1, 2, 63, 127, 129, 257]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", EDGE_N)
+@pytest.mark.parametrize("causal", [False, True])
+def test_edge_lengths_bf16(N, d, causal):
+    q, k, v, do = make_qkvdo(1, 2, N, d, "bf16", seed=10 + N)
+    full_parity(q, k, v, do, default_scale(d), causal, None, "bf16")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 63, 129])
+@pytest.mark.parametrize("causal", [False, True])
+def test_edge_lengths_f32(N, d, causal):
+    q, k, v, do = make_qkvdo(1, 2, N, d, "f32", seed=20 + N)
+    full_parity(q, k, v, do, default_scale(d), causal, None, "f32")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged_multi_tile(d, causal):
+    """Several query and key tiles with a ragged tail, two batches, three heads."""
+    q, k, v, do = make_qkvdo(2, 3, 1000, d, "bf16", seed=3)
+    full_parity(q, k, v, do, default_scale(d), causal, None, "bf16")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1000, 1024])
+def test_block_mask(d, causal, N):
+    q, k, v, do = make_qkvdo(1, 2, N, d, "bf16", seed=4)
+    mask = make_blockmask(N, frac=0.3, seed=5)
+    full_parity(q, k, v, do, default_scale(d), causal, mask, "bf16")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_block_mask_with_empty_rows(dtype):
+    """A user mask without the diagonal: rows of an all-zero mask row must give
+    O = 0, lse = -inf and zero gradients, never NaN."""
+    N, d = 600, 64
+    q, k, v, do = make_qkvdo(1, 2, N, d, dtype, seed=6)
+    mask = make_random_blockmask(N, 0.4, seed=7, diagonal=False)
+    mask[1, :] = 0
+    got = full_parity(q, k, v, do, default_scale(d), False, mask, dtype)
+    assert torch.all(got["o"][:, :, 128:256] == 0)
+    assert torch.all(torch.isneginf(got["lse"][:, :, 128:256]))
+    assert torch.all(got["dq"][:, :, 128:256] == 0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("scale", [-0.3, 0.0, 0.5])
+def test_other_scales(dtype, scale):
+    q, k, v, do = make_qkvdo(1, 2, 300, 64, dtype, seed=8)
+    full_parity(q, k, v, do, scale, True, None, dtype)
+
+
+def test_f32_with_block_mask():
+    q, k, v, do = make_qkvdo(1, 2, 400, 128, "f32", seed=9)
+    mask = make_blockmask(400, frac=0.5, seed=1)
+    full_parity(q, k, v, do, default_scale(128), True, mask, "f32")
+
+
+# ---- determinism -------------------------------------------------------------------
+@pytest.mark.parametrize("d", [64, 128])
+def test_bitwise_repeatable(d):
+    import exact_io_aware_18_amd as fa
+
+    dev = device()
+    q, k, v, do = (t.to(dev) for t in make_qkvdo(2, 4, 777, d, "bf16", seed=11))
+    scale = default_scale(d)
+    o1, l1 = fa.fwd(q, k, v, scale, True)
+    g1 = fa.bwd(q, k, v, o1, l1, do, scale, True)
+    o2, l2 = fa.fwd(q, k, v, scale, True)
+    g2 = fa.bwd(q, k, v, o2, l2, do, scale, True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
+def test_row_shift_on_gpu():
+    """Scores shifted by a per-row constant (through a column of ones in K and a
+    change of Q's last column) leave O unchanged and shift lse by the constant."""
+    import exact_io_aware_18_amd as fa
+
+    dev = device()
+    N, d = 512, 64
+    q, k, v, _ = make_qkvdo(1, 2, N, d, "bf16", seed=12)
+    k[..., d - 1] = 1.0
+    q[..., d - 1] = 0.0
+    shift = torch.randint(-4, 5, (1, 2, N)).to(torch.bfloat16)  # exact in bf16
+    q2 = q.clone()
+    q2[..., d - 1] = shift
+    scale = 0.125  # a power of two keeps scale * shift exact
+    o1, l1 = fa.fwd(q.to(dev), k.to(dev), v.to(dev), scale, True)
+    o2, l2 = fa.fwd(q2.to(dev), k.to(dev), v.to(dev), scale, True)
+    torch.cuda.synchronize()
+    assert (o1.float() - o2.float()).abs().max().item() <= 2e-2
+    exp_shift = scale * shift.float().to(dev)
+    assert (l2 - l1 - exp_shift).abs().max().item() <= 1e-3
