@@ -3,10 +3,11 @@
 // enqueues nothing and is testable without a GPU.
 #include <hip/hip_runtime.h>
 
+#include <cfloat>
 #include <cmath>
 #include <cstdint>
 
-#include "../../include/fa.h"
+#include "fa.h"
 #include "fa_bwd.h"
 #include "fa_f32.h"
 #include "fa_fwd.h"
@@ -260,7 +261,9 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   a.nqt = (N + 127) / 128;
   a.total = B * H * a.nqt;
   a.nb = nblocks(N);
-  a.c = std::fabs(scale) * fa::kLog2e;
+  // c > 0 even for scale == 0, so masked scores (-inf) stay -inf after the
+  // scaling; FLT_MIN times a finite score rounds 2^(score) to exactly 1.
+  a.c = std::fmax(std::fabs(scale) * fa::kLog2e, FLT_MIN);
   a.negate_q = scale < 0.f;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();

@@ -50,6 +50,72 @@ __device__ __forceinline__ int swz(int row, int chunk, int nchunk) {
   return chunk ^ (f & (nchunk - 1));
 }
 
+// Swizzle of a natural [rows][D] bf16 tile whose rows are read as MFMA
+// operands with ds_read_b128 in perm32 row order: chunk ^ kswz(row) keeps
+// every 16 consecutive lanes on distinct LDS banks for 128- and 256-byte rows.
+template <int D>
+__device__ __forceinline__ int kswz(int row) {
+  if (D == 64) return (row >> 1) & 7;
+  const int b3 = (row >> 3) & 1;
+  return ((row & 7) ^ (b3 << 2)) | (b3 << 3);
+}
+
+// Swizzle of a natural [rows][D] bf16 tile read with ds_read_b64_tr_b16
+// (4 consecutive rows x 32 bytes per 16 lanes): conflict-free for 128- and
+// 256-byte rows.
+template <int D>
+__device__ __forceinline__ int vswz(int row) {
+  return ((((row >> 1) & 1) << 2) | ((row >> 2) & 3) | ((row & 1) << 3)) & (D / 8 - 1);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// Transposed 8-byte LDS read (gfx950 ds_read_b64_tr_b16).  Within each group
+// of 16 lanes, lane i receives element i % 4 of the 8-byte words addressed by
+// lanes i/4, 4 + i/4, 8 + i/4 and 12 + i/4, in that order: if lane 4u + q
+// addresses row u, columns 4q .. 4q+3 of a row-major bf16 block, lane i gets
+// column i of rows 0..3.
+__device__ __forceinline__ bf16x4 lds_read_tr8(const __attribute__((address_space(3))) char* p) {
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+__device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// max over lane l and lane l ^ 32 (v_permlane32_swap)
+__device__ __forceinline__ float xhalf_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// sum over lane l and lane l ^ 32
+__device__ __forceinline__ float xhalf_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Sum of the eight bf16 values of v (as fp32) added to acc: four v_dot2 ops.
+__device__ __forceinline__ float sum8(bf16x8 v, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  float a0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one, acc, false);
+  float a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one, 0.f, false);
+  a0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one, a0, false);
+  a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one, a1, false);
+  return a0 + a1;
+}
+
+// 16-byte direct-to-LDS copy (global_load_lds_dwordx4): lane l of the wave
+// writes its 16 bytes at lds + 16*l; lds must be wave-uniform.
+__device__ __forceinline__ void lds_dma16(const void* src, char* lds) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
 __device__ __forceinline__ bf16x8 lds_read16(const char* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }

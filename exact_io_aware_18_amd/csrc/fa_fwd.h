@@ -2,29 +2,31 @@
 //
 // One workgroup owns 128 query rows of one (batch, head); each of its four
 // waves owns 32 of them and keeps its Q fragment in registers for the whole
-// kernel.  K/V tiles of 64 keys are streamed HBM -> registers -> LDS with
-// one tile of prefetch and two LDS buffers, so each iteration needs a single
-// barrier ("Tiling": blocks of Q, K, V are loaded from HBM to on-chip memory
-// and the output is accumulated block by block, "FlashAttention: Fast and
+// kernel.  K/V tiles of 64 keys are copied HBM -> LDS by direct-to-LDS loads
+// (global_load_lds_dwordx4) into two buffers, so the copy of tile t+1 runs
+// behind the arithmetic of tile t and each tile costs a single barrier
+// ("Tiling": blocks of Q, K, V are loaded from HBM to on-chip memory and the
+// output is accumulated block by block, "FlashAttention: Fast and
 // Memory-Efficient Exact Attention with IO-Awareness", summary page, §3
 // Method).
 //
 // Per key tile and wave:
-//   S^T = K Q^T on MFMA 32x32x16 bf16 (keys are accumulator rows, the
+//   S^T = K Q^T on MFMA 32x32x16 bf16.  Keys are accumulator rows and the
 //         wave's 32 queries are accumulator columns, so a lane holds 16
-//         scores of one query row per 32 keys and the row max / row sum are
-//         register reductions plus one exchange with lane l^32);
-//   online softmax in the log2 domain with a lazily updated reference max
-//         (the running max is replaced, and O and l rescaled, only when a new
-//         row max exceeds it by more than kLazyTau; the final O / l uses the
-//         same reference, so the result is unchanged) ("Softmax rescaling":
-//         the normalisation is computed incrementally across blocks, §3);
-//   O^T += V^T P^T on MFMA, with P converted to bf16 straight from the score
-//         registers (perm32 row order makes the score registers the MFMA
-//         B operand as they stand).
-// Only O (bf16) and lse (fp32, natural log) are written (Figure 1 caption
-// of "No More Quadratic Complexity for Transformers: Discover the Power of
-// Flash Attention!": the N x N matrix never goes to HBM).
+//         scores of one query row per 32 keys: the row max and row sum are
+//         register reductions plus one exchange with lane l^32.
+//   online softmax in the log2 domain with a lazily updated reference max:
+//         the reference (and O and l with it) moves only when a new row max
+//         exceeds it by more than kLazyTau; O / l uses the same reference, so
+//         the result is unchanged ("Softmax rescaling": the normalisation is
+//         computed incrementally across blocks, §3).
+//   O^T += V^T P^T on MFMA.  P goes to bf16 straight from the score
+//         registers (perm32 row order makes them the B operand as they
+//         stand); V^T comes from the natural V tile through transposed LDS
+//         reads.
+// Only O (bf16) and lse (fp32, natural log) are written (Figure 1 caption of
+// "No More Quadratic Complexity for Transformers: Discover the Power of Flash
+// Attention!": the N x N matrix never goes to HBM).
 #pragma once
 
 #include "fa_device.h"
@@ -45,7 +47,7 @@ struct FwdArgs {
   int nqt;              // query tiles per head
   int total;            // workgroups in the grid
   int nb;               // mask blocks per side
-  float c;              // |scale| * log2(e)
+  float c;              // max(|scale| * log2(e), FLT_MIN): masked scores stay -inf
   int negate_q;         // scale < 0: scores computed with -Q and |scale|
 };
 
@@ -55,21 +57,69 @@ struct FwdTile {
   static constexpr int NT = 64 * NW;
   static constexpr int BR = 32 * NW;     // 128 query rows per workgroup
   static constexpr int BC = 64;          // keys per tile
-  static constexpr int K_BYTES = BC * D * 2;
-  static constexpr int VT_BYTES = D * BC * 2;
-  static constexpr int STAGE = K_BYTES + VT_BYTES;
+  static constexpr int PITCH = 2 * D;    // bytes per K or V row in LDS
+  static constexpr int T_BYTES = BC * PITCH;
+  static constexpr int STAGE = 2 * T_BYTES;  // K tile then V tile
+  static constexpr int ROUNDS = T_BYTES / (NT * 16);  // 16-byte copies per thread per tile
   static constexpr int LIST_CAP = 1024;  // mask blocks listed per pass
+};
+
+// Direct-to-LDS copy of one BC-row tile of a [N][D] bf16 matrix into a
+// natural, swizzled LDS tile.  Wave w, round e fills LDS bytes
+// [(e*NW + w) * 1024, +1024), lane l landing at +16*l; that slot holds tile
+// row (e*NW + w) * (1024 / PITCH) + l / CPR, physical chunk l % CPR, i.e.
+// logical chunk (l % CPR) ^ swizzle(row).  The per-lane source offsets are
+// fixed for every tile, so a copy costs one instruction per round.
+template <int D, bool VTILE>
+struct TileCopy {
+  using T = FwdTile<D>;
+  static constexpr int CPR = T::PITCH / 16;
+  int off[T::ROUNDS];  // byte offset of this lane's 16 bytes within the tile
+  int row[T::ROUNDS];  // tile row of this lane's 16 bytes
+
+  __device__ __forceinline__ void init(int w, int lane) {
+#pragma unroll
+    for (int e = 0; e < T::ROUNDS; ++e) {
+      row[e] = (e * T::NW + w) * (1024 / T::PITCH) + lane / CPR;
+      const int logical = (lane % CPR) ^ (VTILE ? vswz<D>(row[e]) : kswz<D>(row[e]));
+      off[e] = row[e] * (2 * D) + logical * 16;
+    }
+  }
+  // rows [row0, row0 + BC) of src; rows past N re-read row N-1 (finite data
+  // that the mask zeroes)
+  __device__ __forceinline__ void issue(char* lds_tile, const __bf16* src, int row0, int N, int w) const {
+    const char* base = reinterpret_cast<const char*>(src + (size_t)row0 * D);
+    if (row0 + T::BC <= N) {
+#pragma unroll
+      for (int e = 0; e < T::ROUNDS; ++e)
+        lds_dma16(base + off[e], lds_tile + (e * T::NW + w) * 1024);
+    } else {
+      const int over = (N - 1 - row0) * (2 * D);  // byte offset of row N-1
+#pragma unroll
+      for (int e = 0; e < T::ROUNDS; ++e) {
+        const int o = (row0 + row[e] < N) ? off[e] : over + (off[e] - row[e] * (2 * D));
+        lds_dma16(base + o, lds_tile + (e * T::NW + w) * 1024);
+      }
+    }
+  }
 };
 
 template <int D, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   using T = FwdTile<D>;
-  constexpr int BC = T::BC, BR = T::BR, NT = T::NT;
-  __shared__ __attribute__((aligned(16))) char smem[2 * T::STAGE];
+  constexpr int BC = T::BC, BR = T::BR, NT = T::NT, PITCH = T::PITCH;
+  constexpr int NKC = D / 16;  // k-steps of S^T = K Q^T
+  constexpr int NCT = D / 32;  // 32-row tiles of O^T
+  // Two separate buffers (not one array indexed by t & 1): the compiler can
+  // then prove that the copy into one does not alias reads of the other and
+  // does not wait for the copy before reading.
+  __shared__ __attribute__((aligned(1024))) char buf0[T::STAGE];
+  __shared__ __attribute__((aligned(1024))) char buf1[T::STAGE];
   __shared__ int blist[MASK ? T::LIST_CAP : 1];
   __shared__ int wcount[T::NW];
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in an SGPR
   const int h = lane >> 5, li = lane & 31;
 
   const int g = xcd_remap(blockIdx.x, a.total);
@@ -82,30 +132,125 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   const __bf16* Kh = a.k + head;
   const __bf16* Vh = a.v + head;
   const int q0 = qt * BR;
-  const int qw0 = q0 + 32 * w;       // first query of this wave
-  const int qi = qw0 + li;           // this lane's query row
+  const int qw0 = q0 + 32 * w;  // first query of this wave
+  const int qi = qw0 + li;      // this lane's query row
 
   // Q^T fragments (B operand): lane supplies Q[qi][16kc + 8h .. +7].
-  bf16x8 qf[D / 16];
+  bf16x8 qf[NKC];
 #pragma unroll
-  for (int kc = 0; kc < D / 16; ++kc) {
+  for (int kc = 0; kc < NKC; ++kc) {
     u32x4 x = u32x4{0u, 0u, 0u, 0u};
     if (qi < N) x = gload16(Qh + (size_t)qi * D + 16 * kc + 8 * h);
     if (a.negate_q) x ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
     qf[kc] = __builtin_bit_cast(bf16x8, x);
   }
 
-  f32x16 o[D / 32];
+  // Per-lane LDS offsets, fixed for every tile.
+  // K operand (A of S^T): row perm32(li) (+32 for the second key half), chunk 2kc+h.
+  const int krow = perm32(li);
+  int koff[NKC];
 #pragma unroll
-  for (int ct = 0; ct < D / 32; ++ct) o[ct] = f32x16{};
+  for (int kc = 0; kc < NKC; ++kc) koff[kc] = krow * PITCH + (((2 * kc + h) ^ kswz<D>(krow)) << 4);
+  // V^T operand (A of O^T) by transposed reads: for read r of k-step kc and
+  // O^T tile ct, lane l addresses key row 16kc + 8h + 4r + (l%16)/4 and
+  // columns 32ct + perm32(16*((l/16)%2) + 4*(l%4)) .. +3.
+  const int vrow = 8 * h + ((lane & 15) >> 2);
+  const int vcl = 2 * ((lane >> 4) & 1) + (lane & 1);  // 16-byte chunk within a 32-column group
+  int voff[NCT][2];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int row = vrow + 4 * r;
+      voff[ct][r] = T::T_BYTES + row * PITCH + (((4 * ct + vcl) ^ vswz<D>(row)) << 4) + ((lane >> 1) & 1) * 8;
+    }
+
+  f32x16 o[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) o[ct] = f32x16{};
   float Mref = -INFINITY;  // reference max (log2 units), identical in both halves
   float L = 0.f;           // partial row sum over this lane's keys
 
   const int ntiles_all = (N + BC - 1) / BC;
   const float c = a.c;
+  TileCopy<D, false> kcopy;
+  TileCopy<D, true> vcopy;
+  kcopy.init(w, lane);
+  vcopy.init(w, lane);
 
-  StageRows16<BC, D, NT> ks;
-  StageBlocks4<BC, D, NT> vs;
+  // One key tile from LDS buffer `st`.
+  auto compute = [&] __device__ (const char* st, int k0) {
+    // ---- S^T = K Q^T for the two 32-key halves of the tile; every K
+    // operand is requested before the first product
+    bf16x8 ka0[NKC], ka1[NKC];
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      ka0[kc] = lds_read16(st + koff[kc]);
+      ka1[kc] = lds_read16(st + koff[kc] + 32 * PITCH);
+    }
+    f32x16 s0 = f32x16{}, s1 = f32x16{};
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      s0 = mfma32(ka0[kc], qf[kc], s0);
+      s1 = mfma32(ka1[kc], qf[kc], s1);
+    }
+    // ---- mask (only tiles that cross the diagonal or the sequence end)
+    const bool edge = (CAUSAL && k0 + BC - 1 > qw0) || (k0 + BC > N);
+    if (edge) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key0 = k0 + acc_row(r, h), key1 = key0 + 32;
+        if ((CAUSAL && key0 > qi) || key0 >= N) s0[r] = -INFINITY;
+        if ((CAUSAL && key1 > qi) || key1 >= N) s1[r] = -INFINITY;
+      }
+    }
+    // ---- row max over the tile, shared by both halves
+    float m4[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      m4[u] = fmaxf(fmaxf(fmaxf(s0[4 * u], s0[4 * u + 1]), fmaxf(s0[4 * u + 2], s0[4 * u + 3])),
+                    fmaxf(fmaxf(s1[4 * u], s1[4 * u + 1]), fmaxf(s1[4 * u + 2], s1[4 * u + 3])));
+    float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+    mx = xhalf_max(mx);
+    const float mt = (mx == -INFINITY) ? -INFINITY : mx * c;
+    const bool need = mt > Mref + kLazyTau;
+    if (wave_any(need)) {
+      const float Mn = need ? mt : Mref;
+      const float alpha = need ? __builtin_amdgcn_exp2f(Mref - Mn) : 1.f;
+      L *= alpha;
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) o[ct] *= alpha;
+      Mref = Mn;
+    }
+    const float mb = (Mref == -INFINITY) ? 0.f : Mref;
+    // ---- P = 2^(S*c - Mref); l sums P in fp32 (a tree, not a serial chain),
+    // the products take P rounded to bf16
+    bf16x8 pb[4];
+    float lsum[4];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      float p0[8], p1[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p0[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[8 * hh + e], c, -mb));
+        p1[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[8 * hh + e], c, -mb));
+      }
+      pb[hh] = to_bf16x8(p0[0], p0[1], p0[2], p0[3], p0[4], p0[5], p0[6], p0[7]);
+      pb[2 + hh] = to_bf16x8(p1[0], p1[1], p1[2], p1[3], p1[4], p1[5], p1[6], p1[7]);
+      lsum[hh] = ((p0[0] + p0[1]) + (p0[2] + p0[3])) + ((p0[4] + p0[5]) + (p0[6] + p0[7]));
+      lsum[2 + hh] = ((p1[0] + p1[1]) + (p1[2] + p1[3])) + ((p1[4] + p1[5]) + (p1[6] + p1[7]));
+    }
+    L += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+    // ---- O^T += V^T P^T
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int kc = 0; kc < BC / 16; ++kc) {
+        const auto* base = (const __attribute__((address_space(3))) char*)(st + 16 * kc * PITCH);
+        const bf16x8 av = cat8(lds_read_tr8(base + voff[ct][0]), lds_read_tr8(base + voff[ct][1]));
+        o[ct] = mfma32(av, pb[kc], o[ct]);
+      }
+  };
 
   // Key-tile schedule: a list pass covers mask blocks [cb0, cb1).
   const int qb = q0 >> 7;  // mask row (BR == 128)
@@ -122,114 +267,44 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
       ntiles = 2 * cnt;
       if (cnt > 0 && 2 * blist[cnt - 1] + 1 >= ntiles_all) ntiles -= 1;  // short last block
     }
-    auto tile_of = [&](int t) -> int { return MASK ? 2 * blist[t >> 1] + (t & 1) : t; };
+    auto tile_of = [&] __device__ (int t) -> int { return MASK ? 2 * blist[t >> 1] + (t & 1) : t; };
 
     if (ntiles > 0) {
       const int k0 = tile_of(0) * BC;
-      ks.load(Kh, k0, N, tid);
-      vs.load(Vh, k0, N, tid);
-      ks.store(smem, tid);
-      vs.store_tr(smem + T::K_BYTES, tid);
+      kcopy.issue(buf0, Kh, k0, N, w);
+      vcopy.issue(buf0 + T::T_BYTES, Vh, k0, N, w);
     }
-    if (ntiles > 1) {
-      const int k0 = tile_of(1) * BC;
-      ks.load(Kh, k0, N, tid);
-      vs.load(Vh, k0, N, tid);
-    }
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    for (int t = 0; t < ntiles; ++t) {
-      const char* Ks = smem + (t & 1) * T::STAGE;
-      const char* Vt = Ks + T::K_BYTES;
+    // Tile t is read from one buffer while tile t+1 is copied into the other
+    // (last read in iteration t-1, before that iteration's barrier).
+    auto step = [&] __device__ (const char* cur, char* nxt, int t) {
+      if (t + 1 < ntiles) {
+        const int k1 = tile_of(t + 1) * BC;
+        kcopy.issue(nxt, Kh, k1, N, w);
+        vcopy.issue(nxt + T::T_BYTES, Vh, k1, N, w);
+      }
       const int k0 = tile_of(t) * BC;
       const bool active = qw0 < N && !(CAUSAL && k0 > qw0 + 31);
-      if (active) {
-        // ---- S^T = K Q^T for two 32-key halves of the tile
-        f32x16 s[2];
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          s[t2] = f32x16{};
-          const int row = 32 * t2 + perm32(li);
-#pragma unroll
-          for (int kc = 0; kc < D / 16; ++kc)
-            s[t2] = mfma32(tile_read<2 * D>(Ks, row, 2 * kc + h), qf[kc], s[t2]);
-        }
-        // ---- mask (only tiles that cross the diagonal or the sequence end)
-        const bool edge = (CAUSAL && k0 + BC - 1 > qw0) || (k0 + BC > N);
-        if (edge) {
-#pragma unroll
-          for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = k0 + 32 * t2 + acc_row(r, h);
-              if ((CAUSAL && key > qi) || key >= N) s[t2][r] = -INFINITY;
-            }
-        }
-        // ---- row max over the tile, shared by both halves
-        float mx = -INFINITY;
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t2][r]);
-        mx = fmaxf(mx, xhalf(mx));
-        const float mt = (mx == -INFINITY) ? -INFINITY : mx * c;
-        const bool need = mt > Mref + kLazyTau;
-        if (wave_any(need)) {
-          const float Mn = need ? mt : Mref;
-          const float alpha = need ? __builtin_amdgcn_exp2f(Mref - Mn) : 1.f;
-          L *= alpha;
-#pragma unroll
-          for (int ct = 0; ct < D / 32; ++ct) o[ct] *= alpha;
-          Mref = Mn;
-        }
-        const float mb = (Mref == -INFINITY) ? 0.f : Mref;
-        // ---- P = 2^(S*c - Mref) as bf16; l accumulates the same values
-        bf16x8 pb[4];
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          float p[16];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t2][r], c, -mb));
-            if (edge) x = (s[t2][r] == -INFINITY) ? 0.f : x;
-            p[r] = x;
-            L += x;
-          }
-          pb[2 * t2 + 0] = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-          pb[2 * t2 + 1] = to_bf16x8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
-        }
-        // ---- O^T += V^T P^T
-#pragma unroll
-        for (int ct = 0; ct < D / 32; ++ct) {
-          const int row = 32 * ct + perm32(li);
-#pragma unroll
-          for (int kc = 0; kc < BC / 16; ++kc)
-            o[ct] = mfma32(tile_read<2 * BC>(Vt, row, 2 * kc + h), pb[kc], o[ct]);
-        }
-      }
-      // ---- stage tile t+1 into the other buffer, prefetch tile t+2
-      if (t + 1 < ntiles) {
-        char* nb = smem + ((t + 1) & 1) * T::STAGE;
-        ks.store(nb, tid);
-        vs.store_tr(nb + T::K_BYTES, tid);
-      }
-      if (t + 2 < ntiles) {
-        const int k2 = tile_of(t + 2) * BC;
-        ks.load(Kh, k2, N, tid);
-        vs.load(Vh, k2, N, tid);
-      }
+      if (active) compute(cur, k0);
+      __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
+    };
+    for (int t = 0; t < ntiles; t += 2) {
+      step(buf0, buf1, t);
+      if (t + 1 < ntiles) step(buf1, buf0, t + 1);
     }
   }
 
   // ---- epilogue: O = O / l, lse = (Mref + log2 l) * ln 2
-  const float Lt = L + xhalf(L);
+  const float Lt = xhalf_sum(L);
   if (qi < N) {
     const bool empty = !(Lt > 0.f);
     const float inv = empty ? 0.f : 1.f / Lt;
     __bf16* Orow = a.o + head + (size_t)qi * D;
 #pragma unroll
-    for (int ct = 0; ct < D / 32; ++ct)
+    for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const int col = 32 * ct + 16 * hh + 8 * h;
