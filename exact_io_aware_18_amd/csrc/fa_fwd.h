@@ -36,6 +36,11 @@ namespace fa {
 
 constexpr float kLazyTau = 8.0f;  // log2 units: P values stay below 2^8
 
+// instruction classes for __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedValu = 0x002;
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
 struct FwdArgs {
   const __bf16* q;
   const __bf16* k;
@@ -62,6 +67,12 @@ struct FwdTile {
   static constexpr int STAGE = 2 * T_BYTES;  // K tile then V tile
   static constexpr int ROUNDS = T_BYTES / (NT * 16);  // 16-byte copies per thread per tile
   static constexpr int LIST_CAP = 1024;  // mask blocks listed per pass
+  // Two workgroups per CU (two waves per SIMD): one wave's softmax overlaps
+  // the other's products.  At d=64 a wave also keeps the scores of the next
+  // tile in flight (PIPE); at d=128 that does not fit in the 256 registers a
+  // wave has at this occupancy.
+  static constexpr int MIN_WG = 2;
+  static constexpr bool PIPE = (D == 64);
 };
 
 // Direct-to-LDS copy of one BC-row tile of a [N][D] bf16 matrix into a
@@ -74,15 +85,15 @@ template <int D, bool VTILE>
 struct TileCopy {
   using T = FwdTile<D>;
   static constexpr int CPR = T::PITCH / 16;
-  int off[T::ROUNDS];  // byte offset of this lane's 16 bytes within the tile
-  int row[T::ROUNDS];  // tile row of this lane's 16 bytes
+  uint32_t off[T::ROUNDS];  // byte offset of this lane's 16 bytes within the tile
+  int row[T::ROUNDS];       // tile row of this lane's 16 bytes
 
   __device__ __forceinline__ void init(int w, int lane) {
 #pragma unroll
     for (int e = 0; e < T::ROUNDS; ++e) {
       row[e] = (e * T::NW + w) * (1024 / T::PITCH) + lane / CPR;
       const int logical = (lane % CPR) ^ (VTILE ? vswz<D>(row[e]) : kswz<D>(row[e]));
-      off[e] = row[e] * (2 * D) + logical * 16;
+      off[e] = (uint32_t)(row[e] * (2 * D) + logical * 16);
     }
   }
   // rows [row0, row0 + BC) of src; rows past N re-read row N-1 (finite data
@@ -94,10 +105,10 @@ struct TileCopy {
       for (int e = 0; e < T::ROUNDS; ++e)
         lds_dma16(base + off[e], lds_tile + (e * T::NW + w) * 1024);
     } else {
-      const int over = (N - 1 - row0) * (2 * D);  // byte offset of row N-1
+      const uint32_t over = (uint32_t)((N - 1 - row0) * (2 * D));  // byte offset of row N-1
 #pragma unroll
       for (int e = 0; e < T::ROUNDS; ++e) {
-        const int o = (row0 + row[e] < N) ? off[e] : over + (off[e] - row[e] * (2 * D));
+        const uint32_t o = (row0 + row[e] < N) ? off[e] : over + (off[e] - (uint32_t)(row[e] * (2 * D)));
         lds_dma16(base + o, lds_tile + (e * T::NW + w) * 1024);
       }
     }
@@ -105,16 +116,19 @@ struct TileCopy {
 };
 
 template <int D, bool CAUSAL, bool MASK>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
+__global__ __launch_bounds__(256, FwdTile<D>::MIN_WG) void fwd_bf16_kernel(FwdArgs a) {
   using T = FwdTile<D>;
   constexpr int BC = T::BC, BR = T::BR, NT = T::NT, PITCH = T::PITCH;
   constexpr int NKC = D / 16;  // k-steps of S^T = K Q^T
   constexpr int NCT = D / 32;  // 32-row tiles of O^T
-  // Two separate buffers (not one array indexed by t & 1): the compiler can
-  // then prove that the copy into one does not alias reads of the other and
-  // does not wait for the copy before reading.
-  __shared__ __attribute__((aligned(1024))) char buf0[T::STAGE];
-  __shared__ __attribute__((aligned(1024))) char buf1[T::STAGE];
+  // K runs one tile ahead of V: while tile t is normalised and multiplied
+  // with V(t), S(t+1) = K(t+1) Q^T is already in the matrix pipe.  Four
+  // separate buffers (not arrays indexed by t & 1) let the compiler prove
+  // that a copy into one does not alias reads of another.
+  __shared__ __attribute__((aligned(1024))) char kb0[T::T_BYTES];
+  __shared__ __attribute__((aligned(1024))) char kb1[T::T_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vb0[T::T_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vb1[T::T_BYTES];
   __shared__ int blist[MASK ? T::LIST_CAP : 1];
   __shared__ int wcount[T::NW];
 
@@ -162,7 +176,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int row = vrow + 4 * r;
-      voff[ct][r] = T::T_BYTES + row * PITCH + (((4 * ct + vcl) ^ vswz<D>(row)) << 4) + ((lane >> 1) & 1) * 8;
+      voff[ct][r] = row * PITCH + (((4 * ct + vcl) ^ vswz<D>(row)) << 4) + ((lane >> 1) & 1) * 8;
     }
 
   f32x16 o[NCT];
@@ -178,22 +192,37 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   kcopy.init(w, lane);
   vcopy.init(w, lane);
 
-  // One key tile from LDS buffer `st`.
-  auto compute = [&] __device__ (const char* st, int k0) {
-    // ---- S^T = K Q^T for the two 32-key halves of the tile; every K
-    // operand is requested before the first product
+  // S^T = K Q^T for the two 32-key halves of the tile in `kt`.
+  auto scores = [&] __device__ (const char* kt, f32x16& s0, f32x16& s1) {
     bf16x8 ka0[NKC], ka1[NKC];
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) {
-      ka0[kc] = lds_read16(st + koff[kc]);
-      ka1[kc] = lds_read16(st + koff[kc] + 32 * PITCH);
+      ka0[kc] = lds_read16(kt + koff[kc]);
+      ka1[kc] = lds_read16(kt + koff[kc] + 32 * PITCH);
     }
-    f32x16 s0 = f32x16{}, s1 = f32x16{};
+    s0 = f32x16{};
+    s1 = f32x16{};
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) {
       s0 = mfma32(ka0[kc], qf[kc], s0);
       s1 = mfma32(ka1[kc], qf[kc], s1);
     }
+    // K reads run three k-steps ahead of their products
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 0);
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+      if (kc + 3 < NKC) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+    }
+  };
+
+  // One pipelined step on the tile at key k0, whose scores are in s0/s1:
+  // mask, row max and (rarely) the rescale of O and l first; then, in one
+  // scheduling region, the products S(next) = K(next) Q^T go to the matrix
+  // pipe interleaved with P = 2^(S*c - Mref), its bf16 copy and its fp32 row
+  // sum on the VALU; finally O^T += V^T P^T with V from `vt`.
+  auto softmax_pv = [&] __device__ (f32x16 s0, f32x16 s1, const char* vt, int k0,
+                                    const char* knext, f32x16& n0, f32x16& n1) {
     // ---- mask (only tiles that cross the diagonal or the sequence end)
     const bool edge = (CAUSAL && k0 + BC - 1 > qw0) || (k0 + BC > N);
     if (edge) {
@@ -204,14 +233,14 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
         if ((CAUSAL && key1 > qi) || key1 >= N) s1[r] = -INFINITY;
       }
     }
-    // ---- row max over the tile, shared by both halves
-    float m4[4];
+    // ---- row max over the tile (v_max3 chains), shared by both halves
+    float m0 = fmaxf(s0[0], s0[1]), m1 = fmaxf(s1[0], s1[1]);
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      m4[u] = fmaxf(fmaxf(fmaxf(s0[4 * u], s0[4 * u + 1]), fmaxf(s0[4 * u + 2], s0[4 * u + 3])),
-                    fmaxf(fmaxf(s1[4 * u], s1[4 * u + 1]), fmaxf(s1[4 * u + 2], s1[4 * u + 3])));
-    float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
-    mx = xhalf_max(mx);
+    for (int r = 2; r < 16; r += 2) {
+      m0 = fmaxf(fmaxf(m0, s0[r]), s0[r + 1]);
+      m1 = fmaxf(fmaxf(m1, s1[r]), s1[r + 1]);
+    }
+    const float mx = xhalf_max(fmaxf(m0, m1));
     const float mt = (mx == -INFINITY) ? -INFINITY : mx * c;
     const bool need = mt > Mref + kLazyTau;
     if (wave_any(need)) {
@@ -223,7 +252,23 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
       Mref = Mn;
     }
     const float mb = (Mref == -INFINITY) ? 0.f : Mref;
-    // ---- P = 2^(S*c - Mref); l sums P in fp32 (a tree, not a serial chain),
+    // ---- S(next) on the matrix pipe ...
+    if constexpr (T::PIPE) {
+      bf16x8 ka0[NKC], ka1[NKC];
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        ka0[kc] = lds_read16(knext + koff[kc]);
+        ka1[kc] = lds_read16(knext + koff[kc] + 32 * PITCH);
+      }
+      n0 = f32x16{};
+      n1 = f32x16{};
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        n0 = mfma32(ka0[kc], qf[kc], n0);
+        n1 = mfma32(ka1[kc], qf[kc], n1);
+      }
+    }
+    // ---- ... while P = 2^(S*c - Mref) and l (fp32 tree) run on the VALU;
     // the products take P rounded to bf16
     bf16x8 pb[4];
     float lsum[4];
@@ -241,15 +286,34 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
       lsum[2 + hh] = ((p1[0] + p1[1]) + (p1[2] + p1[3])) + ((p1[4] + p1[5]) + (p1[6] + p1[7]));
     }
     L += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
-    // ---- O^T += V^T P^T
+    if constexpr (T::PIPE) {
+      // interleave: K reads three k-steps ahead, one MFMA per ~7 VALU ops
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 1);
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(kSchedValu, 112 / (2 * NKC), 1);
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(kSchedValu, 112 / (2 * NKC), 1);
+        if (kc + 3 < NKC) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 1);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- O^T += V^T P^T, V reads two products ahead
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
       for (int kc = 0; kc < BC / 16; ++kc) {
-        const auto* base = (const __attribute__((address_space(3))) char*)(st + 16 * kc * PITCH);
+        const auto* base = (const __attribute__((address_space(3))) char*)(vt + 16 * kc * PITCH);
         const bf16x8 av = cat8(lds_read_tr8(base + voff[ct][0]), lds_read_tr8(base + voff[ct][1]));
         o[ct] = mfma32(av, pb[kc], o[ct]);
       }
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 2);
+#pragma unroll
+    for (int m = 0; m < NCT * BC / 16; ++m) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 2);
+      if (m + 2 < NCT * BC / 16) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 2);
+    }
   };
 
   // Key-tile schedule: a list pass covers mask blocks [cb0, cb1).
@@ -268,33 +332,46 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
       if (cnt > 0 && 2 * blist[cnt - 1] + 1 >= ntiles_all) ntiles -= 1;  // short last block
     }
     auto tile_of = [&] __device__ (int t) -> int { return MASK ? 2 * blist[t >> 1] + (t & 1) : t; };
+    auto active = [&] __device__ (int k0) -> bool { return qw0 < N && !(CAUSAL && k0 > qw0 + 31); };
+    if (ntiles == 0) continue;
 
-    if (ntiles > 0) {
-      const int k0 = tile_of(0) * BC;
-      kcopy.issue(buf0, Kh, k0, N, w);
-      vcopy.issue(buf0 + T::T_BYTES, Vh, k0, N, w);
-    }
+    // prologue: K(0), V(0) (and with PIPE K(1) and S(0))
+    kcopy.issue(kb0, Kh, tile_of(0) * BC, N, w);
+    vcopy.issue(vb0, Vh, tile_of(0) * BC, N, w);
+    if (T::PIPE && ntiles > 1) kcopy.issue(kb1, Kh, tile_of(1) * BC, N, w);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    f32x16 sa0, sa1, sb0, sb1;  // scores of the even / odd tiles
+    if (T::PIPE && active(tile_of(0) * BC)) scores(kb0, sa0, sa1);
 
-    // Tile t is read from one buffer while tile t+1 is copied into the other
-    // (last read in iteration t-1, before that iteration's barrier).
-    auto step = [&] __device__ (const char* cur, char* nxt, int t) {
-      if (t + 1 < ntiles) {
-        const int k1 = tile_of(t + 1) * BC;
-        kcopy.issue(nxt, Kh, k1, N, w);
-        vcopy.issue(nxt + T::T_BYTES, Vh, k1, N, w);
-      }
-      const int k0 = tile_of(t) * BC;
-      const bool active = qw0 < N && !(CAUSAL && k0 > qw0 + 31);
-      if (active) compute(cur, k0);
+    // Iteration t: K(t+1) and V(t) have landed (barrier); copy K(t+2) into
+    // the buffer S(t) was read from and V(t+1) into the one PV(t-1) read;
+    // S(t+1) goes to the matrix pipe, then softmax(t) and PV(t).
+    auto step = [&] __device__ (int t, char* kcur, const char* knext, const char* vcur, char* vnext,
+                                f32x16& scur0, f32x16& scur1, f32x16& snext0, f32x16& snext1) {
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
+      if (T::PIPE) {
+        if (t + 2 < ntiles) kcopy.issue(kcur, Kh, tile_of(t + 2) * BC, N, w);
+      } else {
+        if (t + 1 < ntiles) kcopy.issue(const_cast<char*>(knext), Kh, tile_of(t + 1) * BC, N, w);
+      }
+      if (t + 1 < ntiles) vcopy.issue(vnext, Vh, tile_of(t + 1) * BC, N, w);
+      // a wave with no visible key in tile t has none in later tiles either;
+      // at the last tile S(next) reads a stale buffer and is never used
+      const int k0 = tile_of(t) * BC;
+      if (active(k0)) {
+        if (!T::PIPE) scores(kcur, scur0, scur1);
+        softmax_pv(scur0, scur1, vcur, k0, knext, snext0, snext1);
+      }
     };
     for (int t = 0; t < ntiles; t += 2) {
-      step(buf0, buf1, t);
-      if (t + 1 < ntiles) step(buf1, buf0, t + 1);
+      step(t, kb0, kb1, vb0, vb1, sa0, sa1, sb0, sb1);
+      if (t + 1 < ntiles) step(t + 1, kb1, kb0, vb1, vb0, sb0, sb1, sa0, sa1);
     }
+    // all reads of this pass are done before the next pass (or nothing) reuses the buffers
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   }
 
   // ---- epilogue: O = O / l, lse = (Mref + log2 l) * ln 2
