@@ -20,6 +20,7 @@
 #pragma once
 
 #include "fa_device.h"
+#include "fa_fwd.h"
 #include "fa_sched.h"
 
 namespace fa {
@@ -66,17 +67,20 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__
 }
 
 // ---- dK, dV: keys outer ----------------------------------------------------
+// One workgroup owns 128 keys (one mask block); each wave keeps the K and V
+// rows of its 32 keys in registers and accumulates dK^T and dV^T in
+// registers.  Query tiles of 64 rows (Q, dO, and per query lse*log2(e) and
+// D) stream through two LDS buffers; Q and dO are read as rows for S = Q K^T
+// and dP = dO V^T and through transposed reads for dK^T += Q^T dS and
+// dV^T += dO^T P.
 template <int D>
 struct DkdvTile {
   static constexpr int NW = 4;
   static constexpr int NT = 64 * NW;
-  static constexpr int BK = 32 * NW;            // 128 keys per workgroup
-  static constexpr int BQ = (D == 64) ? 64 : 32;  // queries per tile
-  static constexpr int T_BYTES = BQ * D * 2;
-  // stage: Q, Q^T, dO, dO^T, lse*log2e, D
-  static constexpr int OFF_Q = 0, OFF_QT = T_BYTES, OFF_DO = 2 * T_BYTES, OFF_DOT = 3 * T_BYTES;
-  static constexpr int OFF_L = 4 * T_BYTES, OFF_D = 4 * T_BYTES + BQ * 4;
-  static constexpr int STAGE = 4 * T_BYTES + 2 * BQ * 4;
+  static constexpr int BK = 32 * NW;  // 128 keys per workgroup
+  static constexpr int BQ = 64;       // queries per tile
+  static constexpr int PITCH = 2 * D;
+  static constexpr int T_BYTES = BQ * PITCH;
   static constexpr int LIST_CAP = 1024;
   static constexpr int MIN_WG = (D == 64) ? 2 : 1;
 };
@@ -84,13 +88,19 @@ struct DkdvTile {
 template <int D, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(256, DkdvTile<D>::MIN_WG) void bwd_dkdv_kernel(BwdArgs a) {
   using T = DkdvTile<D>;
-  constexpr int NT = T::NT, BQ = T::BQ, BK = T::BK;
+  constexpr int NT = T::NT, BQ = T::BQ, BK = T::BK, PITCH = T::PITCH;
+  constexpr int NKC = D / 16, NCT = D / 32;
   constexpr int TPB = 128 / BQ;  // query tiles per mask block
-  __shared__ __attribute__((aligned(16))) char smem[2 * T::STAGE];
+  __shared__ __attribute__((aligned(1024))) char qb0[T::T_BYTES];
+  __shared__ __attribute__((aligned(1024))) char qb1[T::T_BYTES];
+  __shared__ __attribute__((aligned(1024))) char db0[T::T_BYTES];
+  __shared__ __attribute__((aligned(1024))) char db1[T::T_BYTES];
+  __shared__ __attribute__((aligned(16))) float lb0[BQ], lb1[BQ], eb0[BQ], eb1[BQ];
   __shared__ int blist[MASK ? T::LIST_CAP : 1];
   __shared__ int wcount[T::NW];
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, li = lane & 31;
   const int g = xcd_remap(blockIdx.x, a.total);
   const int bh = g / a.ntile;
@@ -101,10 +111,10 @@ __global__ __launch_bounds__(256, DkdvTile<D>::MIN_WG) void bwd_dkdv_kernel(BwdA
   const int kw0 = k0 + 32 * w;
   const int kj = kw0 + li;  // this lane's key
 
-  // K and V fragments (B operands): lane supplies row kj, columns 16kc+8h..+7.
-  bf16x8 kf[D / 16], vf[D / 16];
+  // K and V rows (B operands): lane supplies row kj, columns 16kc+8h..+7.
+  bf16x8 kf[NKC], vf[NKC];
 #pragma unroll
-  for (int kc = 0; kc < D / 16; ++kc) {
+  for (int kc = 0; kc < NKC; ++kc) {
     u32x4 x = u32x4{0u, 0u, 0u, 0u}, y = x;
     if (kj < N) {
       x = gload16(a.k + head + (size_t)kj * D + 16 * kc + 8 * h);
@@ -113,38 +123,103 @@ __global__ __launch_bounds__(256, DkdvTile<D>::MIN_WG) void bwd_dkdv_kernel(BwdA
     kf[kc] = __builtin_bit_cast(bf16x8, x);
     vf[kc] = __builtin_bit_cast(bf16x8, y);
   }
-  f32x16 dk[D / 32], dv[D / 32];
+  f32x16 dk[NCT], dv[NCT];
 #pragma unroll
-  for (int ct = 0; ct < D / 32; ++ct) { dk[ct] = f32x16{}; dv[ct] = f32x16{}; }
+  for (int ct = 0; ct < NCT; ++ct) { dk[ct] = f32x16{}; dv[ct] = f32x16{}; }
 
   const __bf16* Qh = a.q + head;
   const __bf16* dOh = a.dout + head;
   const float* Lh = a.lse + (size_t)bh * N;
   const float* Dh = a.Dw + (size_t)bh * N;
   const float c = a.c;
+  TileOffsets<D> toff;
+  toff.init(lane);
+  TileCopy<BQ, D, NT> cp;  // Q and dO tiles have the same shape
+  cp.init(w, lane);
 
-  StageBlocks4<BQ, D, NT> qs, ds;
-  float lval = 0.f, dval = 0.f;
-  auto load_tile = [&](int q0) {
-    qs.load(Qh, q0, N, tid);
-    ds.load(dOh, q0, N, tid);
-    if (tid < BQ) {
-      const int i = q0 + tid;
-      // an empty row (lse = -inf) must give P = 0, not 2^inf
-      lval = (i < N) ? Lh[i] * kLog2e : 0.f;
-      if (lval == -INFINITY) lval = INFINITY;
-    } else if (tid < 2 * BQ) {
-      const int i = q0 + tid - BQ;
-      dval = (i < N) ? Dh[i] : 0.f;
+  // lse*log2(e) (wave 0) and D (wave 1) of the tile's queries go through
+  // registers: an empty row's lse = -inf becomes +inf so that P = 0.
+  auto load_vec = [&] __device__ (int q0) -> float {
+    const int i = q0 + lane;
+    if (w == 0) {
+      float l = (i < N) ? Lh[i] * kLog2e : 0.f;
+      return (l == -INFINITY) ? INFINITY : l;
     }
+    return (w == 1 && i < N) ? Dh[i] : 0.f;
   };
-  auto store_tile = [&](char* st) {
-    qs.store_nat(st + T::OFF_Q, tid);
-    qs.store_tr(st + T::OFF_QT, tid);
-    ds.store_nat(st + T::OFF_DO, tid);
-    ds.store_tr(st + T::OFF_DOT, tid);
-    if (tid < BQ) reinterpret_cast<float*>(st + T::OFF_L)[tid] = lval;
-    else if (tid < 2 * BQ) reinterpret_cast<float*>(st + T::OFF_D)[tid - BQ] = dval;
+  auto store_vec = [&] __device__ (float* lb, float* eb, float x) {
+    if (w == 0) lb[lane] = x;
+    else if (w == 1) eb[lane] = x;
+  };
+
+  auto compute = [&] __device__ (const char* qt, const char* dt, const float* lt, const float* et, int q0) {
+#pragma unroll
+    for (int sb = 0; sb < BQ / 32; ++sb) {
+      const int qs0 = q0 + 32 * sb;
+      if (CAUSAL && qs0 + 31 < kw0) continue;  // every query precedes every key
+      const char* qs = qt + 32 * sb * PITCH;
+      const char* ds = dt + 32 * sb * PITCH;
+      bf16x8 aq[NKC], ad[NKC];
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        aq[kc] = lds_read16(qs + toff.rows[kc]);
+        ad[kc] = lds_read16(ds + toff.rows[kc]);
+      }
+      f32x16 S = f32x16{}, dP = f32x16{};
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        S = mfma32(aq[kc], kf[kc], S);
+        dP = mfma32(ad[kc], vf[kc], dP);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 3);
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 3);
+        if (kc + 3 < NKC) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 3);
+      }
+      // lane's queries: 32sb + 16*hf + 8h + e, e = 0..7
+      const bool edge = (CAUSAL && qs0 < kw0 + 31) || (qs0 + 32 > N);
+      float p[16], dsv[16];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const f32x4 l0 = *reinterpret_cast<const f32x4*>(lt + 32 * sb + 16 * hf + 8 * h);
+        const f32x4 l1 = *reinterpret_cast<const f32x4*>(lt + 32 * sb + 16 * hf + 8 * h + 4);
+        const f32x4 e0 = *reinterpret_cast<const f32x4*>(et + 32 * sb + 16 * hf + 8 * h);
+        const f32x4 e1 = *reinterpret_cast<const f32x4*>(et + 32 * sb + 16 * hf + 8 * h + 4);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = 8 * hf + e;
+          const float lv = e < 4 ? l0[e] : l1[e - 4];
+          const float dvv = e < 4 ? e0[e] : e1[e - 4];
+          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], c, -lv));
+          if (edge) {
+            const int qq = qs0 + acc_row(r, h);
+            if ((CAUSAL && kj > qq) || qq >= N) pv = 0.f;
+          }
+          p[r] = pv;
+          dsv[r] = pv * (dP[r] - dvv);
+        }
+      }
+      const bf16x8 pb0 = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+      const bf16x8 pb1 = to_bf16x8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
+      const bf16x8 sb0 = to_bf16x8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
+      const bf16x8 sb1 = to_bf16x8(dsv[8], dsv[9], dsv[10], dsv[11], dsv[12], dsv[13], dsv[14], dsv[15]);
+      __builtin_amdgcn_sched_barrier(0);
+      // dV^T += dO^T P and dK^T += Q^T dS (scale applied at the end)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        dv[ct] = mfma32(toff.read_tr(ds, 0, ct), pb0, dv[ct]);
+        dv[ct] = mfma32(toff.read_tr(ds, 1, ct), pb1, dv[ct]);
+        dk[ct] = mfma32(toff.read_tr(qs, 0, ct), sb0, dk[ct]);
+        dk[ct] = mfma32(toff.read_tr(qs, 1, ct), sb1, dk[ct]);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 4);
+#pragma unroll
+      for (int m = 0; m < 4 * NCT; ++m) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 4);
+        if (m + 2 < 4 * NCT) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 4);
+      }
+    }
   };
 
   const int kb = k0 >> 7;  // mask column (BK == 128)
@@ -161,68 +236,34 @@ __global__ __launch_bounds__(256, DkdvTile<D>::MIN_WG) void bwd_dkdv_kernel(BwdA
       ntiles = cnt * TPB;
       if (cnt > 0 && blist[cnt - 1] * TPB + TPB > nqt_all) ntiles -= blist[cnt - 1] * TPB + TPB - nqt_all;
     }
-    auto tile_of = [&](int t) -> int { return MASK ? blist[t / TPB] * TPB + (t % TPB) : first + t; };
+    auto tile_of = [&] __device__ (int t) -> int { return MASK ? blist[t / TPB] * TPB + (t % TPB) : first + t; };
+    if (ntiles == 0) continue;
 
-    if (ntiles > 0) { load_tile(tile_of(0) * BQ); store_tile(smem); }
-    if (ntiles > 1) load_tile(tile_of(1) * BQ);
+    {
+      const int q0 = tile_of(0) * BQ;
+      cp.issue(qb0, Qh, q0, N, w);
+      cp.issue(db0, dOh, q0, N, w);
+      store_vec(lb0, eb0, load_vec(q0));
+    }
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-
-    for (int t = 0; t < ntiles; ++t) {
-      const char* st = smem + (t & 1) * T::STAGE;
-      const int q0 = tile_of(t) * BQ;
-      if (kw0 < N) {
-#pragma unroll
-        for (int sb = 0; sb < BQ / 32; ++sb) {
-          const int qs0 = q0 + 32 * sb;
-          if (CAUSAL && qs0 + 31 < kw0) continue;  // every query precedes every key
-          f32x16 S = f32x16{}, dP = f32x16{};
-          const int row = 32 * sb + perm32(li);
-#pragma unroll
-          for (int kc = 0; kc < D / 16; ++kc) {
-            S = mfma32(tile_read<2 * D>(st + T::OFF_Q, row, 2 * kc + h), kf[kc], S);
-            dP = mfma32(tile_read<2 * D>(st + T::OFF_DO, row, 2 * kc + h), vf[kc], dP);
-          }
-          const float* Ls = reinterpret_cast<const float*>(st + T::OFF_L) + 32 * sb + 8 * h;
-          const float* Ds = reinterpret_cast<const float*>(st + T::OFF_D) + 32 * sb + 8 * h;
-          const bool edge = (CAUSAL && qs0 < kw0 + 31) || (qs0 + 32 > N);
-          float p[16], dsv[16];
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const f32x4 l0 = *reinterpret_cast<const f32x4*>(Ls + 16 * half);
-            const f32x4 l1 = *reinterpret_cast<const f32x4*>(Ls + 16 * half + 4);
-            const f32x4 d0 = *reinterpret_cast<const f32x4*>(Ds + 16 * half);
-            const f32x4 d1 = *reinterpret_cast<const f32x4*>(Ds + 16 * half + 4);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int r = 8 * half + e;
-              const float lv = e < 4 ? l0[e] : l1[e - 4];
-              const float dvv = e < 4 ? d0[e] : d1[e - 4];
-              float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], c, -lv));
-              if (edge) {
-                const int qq = qs0 + acc_row(r, h);
-                if ((CAUSAL && kj > qq) || qq >= N) pv = 0.f;
-              }
-              p[r] = pv;
-              dsv[r] = pv * (dP[r] - dvv);
-            }
-          }
-          const bf16x8 pb0 = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-          const bf16x8 pb1 = to_bf16x8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
-          const bf16x8 sb0 = to_bf16x8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
-          const bf16x8 sb1 = to_bf16x8(dsv[8], dsv[9], dsv[10], dsv[11], dsv[12], dsv[13], dsv[14], dsv[15]);
-#pragma unroll
-          for (int ct = 0; ct < D / 32; ++ct) {
-            const int crow = 32 * ct + perm32(li);
-            dv[ct] = mfma32(tile_read<2 * BQ>(st + T::OFF_DOT, crow, 4 * sb + 0 + h), pb0, dv[ct]);
-            dv[ct] = mfma32(tile_read<2 * BQ>(st + T::OFF_DOT, crow, 4 * sb + 2 + h), pb1, dv[ct]);
-            dk[ct] = mfma32(tile_read<2 * BQ>(st + T::OFF_QT, crow, 4 * sb + 0 + h), sb0, dk[ct]);
-            dk[ct] = mfma32(tile_read<2 * BQ>(st + T::OFF_QT, crow, 4 * sb + 2 + h), sb1, dk[ct]);
-          }
-        }
+    auto step = [&] __device__ (int t, const char* qc, const char* dc, const float* lc, const float* ec,
+                                char* qn, char* dn, float* ln, float* en) {
+      float nv = 0.f;
+      if (t + 1 < ntiles) {
+        const int q1 = tile_of(t + 1) * BQ;
+        cp.issue(qn, Qh, q1, N, w);
+        cp.issue(dn, dOh, q1, N, w);
+        nv = load_vec(q1);
       }
-      if (t + 1 < ntiles) store_tile(smem + ((t + 1) & 1) * T::STAGE);
-      if (t + 2 < ntiles) load_tile(tile_of(t + 2) * BQ);
+      if (kw0 < N) compute(qc, dc, lc, ec, tile_of(t) * BQ);
+      if (t + 1 < ntiles) store_vec(ln, en, nv);
+      __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
+    };
+    for (int t = 0; t < ntiles; t += 2) {
+      step(t, qb0, db0, lb0, eb0, qb1, db1, lb1, eb1);
+      if (t + 1 < ntiles) step(t + 1, qb1, db1, lb1, eb1, qb0, db0, lb0, eb0);
     }
   }
 
@@ -231,7 +272,7 @@ __global__ __launch_bounds__(256, DkdvTile<D>::MIN_WG) void bwd_dkdv_kernel(BwdA
     float* dVrow = a.dv + head + (size_t)kj * D;
     const float sc = a.scale;
 #pragma unroll
-    for (int ct = 0; ct < D / 32; ++ct)
+    for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const int col = 32 * ct + 16 * hh + 8 * h;
@@ -247,28 +288,36 @@ __global__ __launch_bounds__(256, DkdvTile<D>::MIN_WG) void bwd_dkdv_kernel(BwdA
 }
 
 // ---- dQ: queries outer -------------------------------------------------------
+// One workgroup owns 128 queries; each wave keeps Q and dO of its 32 queries
+// in registers and accumulates dQ^T in registers.  K/V tiles of 64 keys
+// stream through two LDS buffers; K is read as rows for S^T = K Q^T and
+// through transposed reads for dQ^T += K^T dS^T; V as rows for dP^T = V dO^T.
 template <int D>
 struct DqTile {
   static constexpr int NW = 4;
   static constexpr int NT = 64 * NW;
   static constexpr int BR = 32 * NW;  // 128 queries per workgroup
   static constexpr int BC = 64;       // keys per tile
-  static constexpr int T_BYTES = BC * D * 2;
-  static constexpr int OFF_K = 0, OFF_KT = T_BYTES, OFF_V = 2 * T_BYTES;
-  static constexpr int STAGE = 3 * T_BYTES;
+  static constexpr int PITCH = 2 * D;
+  static constexpr int T_BYTES = BC * PITCH;
   static constexpr int LIST_CAP = 1024;
-  static constexpr int MIN_WG = (D == 64) ? 2 : 1;
+  static constexpr int MIN_WG = 2;
 };
 
 template <int D, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(256, DqTile<D>::MIN_WG) void bwd_dq_kernel(BwdArgs a) {
   using T = DqTile<D>;
-  constexpr int NT = T::NT, BR = T::BR, BC = T::BC;
-  __shared__ __attribute__((aligned(16))) char smem[2 * T::STAGE];
+  constexpr int NT = T::NT, BR = T::BR, BC = T::BC, PITCH = T::PITCH;
+  constexpr int NKC = D / 16, NCT = D / 32;
+  __shared__ __attribute__((aligned(1024))) char kb0[T::T_BYTES];
+  __shared__ __attribute__((aligned(1024))) char kb1[T::T_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vb0[T::T_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vb1[T::T_BYTES];
   __shared__ int blist[MASK ? T::LIST_CAP : 1];
   __shared__ int wcount[T::NW];
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, li = lane & 31;
   const int g = xcd_remap(blockIdx.x, a.total);
   const int bh = g / a.ntile;
@@ -280,9 +329,9 @@ __global__ __launch_bounds__(256, DqTile<D>::MIN_WG) void bwd_dq_kernel(BwdArgs 
   const int qw0 = q0 + 32 * w;
   const int qi = qw0 + li;
 
-  bf16x8 qf[D / 16], df[D / 16];
+  bf16x8 qf[NKC], df[NKC];
 #pragma unroll
-  for (int kc = 0; kc < D / 16; ++kc) {
+  for (int kc = 0; kc < NKC; ++kc) {
     u32x4 x = u32x4{0u, 0u, 0u, 0u}, y = x;
     if (qi < N) {
       x = gload16(a.q + head + (size_t)qi * D + 16 * kc + 8 * h);
@@ -294,15 +343,66 @@ __global__ __launch_bounds__(256, DqTile<D>::MIN_WG) void bwd_dq_kernel(BwdArgs 
   float lse2 = (qi < N) ? a.lse[(size_t)bh * N + qi] * kLog2e : 0.f;
   if (lse2 == -INFINITY) lse2 = INFINITY;  // empty row: P = 0
   const float Di = (qi < N) ? a.Dw[(size_t)bh * N + qi] : 0.f;
-  f32x16 dq[D / 32];
+  f32x16 dq[NCT];
 #pragma unroll
-  for (int ct = 0; ct < D / 32; ++ct) dq[ct] = f32x16{};
+  for (int ct = 0; ct < NCT; ++ct) dq[ct] = f32x16{};
 
   const __bf16* Kh = a.k + head;
   const __bf16* Vh = a.v + head;
   const float c = a.c;
-  StageBlocks4<BC, D, NT> ks;
-  StageRows16<BC, D, NT> vs;
+  TileOffsets<D> toff;
+  toff.init(lane);
+  TileCopy<BC, D, NT> cp;
+  cp.init(w, lane);
+
+  auto compute = [&] __device__ (const char* kt, const char* vt, int k0) {
+    const bool edge = (CAUSAL && k0 + BC - 1 > qw0) || (k0 + BC > N);
+    bf16x8 dsb[4];
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      bf16x8 ak[NKC], av[NKC];
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        ak[kc] = lds_read16(kt + toff.rows[kc] + 32 * t2 * PITCH);
+        av[kc] = lds_read16(vt + toff.rows[kc] + 32 * t2 * PITCH);
+      }
+      f32x16 S = f32x16{}, dP = f32x16{};
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        S = mfma32(ak[kc], qf[kc], S);
+        dP = mfma32(av[kc], df[kc], dP);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 5);
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 5);
+        if (kc + 3 < NKC) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 5);
+      }
+      float dsv[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], c, -lse2));
+        if (edge) {
+          const int key = k0 + 32 * t2 + acc_row(r, h);
+          if ((CAUSAL && key > qi) || key >= N) pv = 0.f;
+        }
+        dsv[r] = pv * (dP[r] - Di);
+      }
+      dsb[2 * t2 + 0] = to_bf16x8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
+      dsb[2 * t2 + 1] = to_bf16x8(dsv[8], dsv[9], dsv[10], dsv[11], dsv[12], dsv[13], dsv[14], dsv[15]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int kc = 0; kc < BC / 16; ++kc) dq[ct] = mfma32(toff.read_tr(kt, kc, ct), dsb[kc], dq[ct]);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 7);
+#pragma unroll
+    for (int m = 0; m < NCT * BC / 16; ++m) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 7);
+      if (m + 2 < NCT * BC / 16) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 7);
+    }
+  };
 
   const int ntiles_all = (N + BC - 1) / BC;
   const int qb = q0 >> 7;
@@ -319,70 +419,28 @@ __global__ __launch_bounds__(256, DqTile<D>::MIN_WG) void bwd_dq_kernel(BwdArgs 
       ntiles = 2 * cnt;
       if (cnt > 0 && 2 * blist[cnt - 1] + 1 >= ntiles_all) ntiles -= 1;
     }
-    auto tile_of = [&](int t) -> int { return MASK ? 2 * blist[t >> 1] + (t & 1) : t; };
-    auto store_tile = [&](char* st) {
-      ks.store_nat(st + T::OFF_K, tid);
-      ks.store_tr(st + T::OFF_KT, tid);
-      vs.store(st + T::OFF_V, tid);
-    };
+    auto tile_of = [&] __device__ (int t) -> int { return MASK ? 2 * blist[t >> 1] + (t & 1) : t; };
+    auto active = [&] __device__ (int k0) -> bool { return qw0 < N && !(CAUSAL && k0 > qw0 + 31); };
+    if (ntiles == 0) continue;
 
-    if (ntiles > 0) {
-      const int k0 = tile_of(0) * BC;
-      ks.load(Kh, k0, N, tid);
-      vs.load(Vh, k0, N, tid);
-      store_tile(smem);
-    }
-    if (ntiles > 1) {
-      const int k0 = tile_of(1) * BC;
-      ks.load(Kh, k0, N, tid);
-      vs.load(Vh, k0, N, tid);
-    }
+    cp.issue(kb0, Kh, tile_of(0) * BC, N, w);
+    cp.issue(vb0, Vh, tile_of(0) * BC, N, w);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-
-    for (int t = 0; t < ntiles; ++t) {
-      const char* st = smem + (t & 1) * T::STAGE;
+    auto step = [&] __device__ (int t, const char* kc_, const char* vc_, char* kn, char* vn) {
+      if (t + 1 < ntiles) {
+        const int k1 = tile_of(t + 1) * BC;
+        cp.issue(kn, Kh, k1, N, w);
+        cp.issue(vn, Vh, k1, N, w);
+      }
       const int k0 = tile_of(t) * BC;
-      const bool active = qw0 < N && !(CAUSAL && k0 > qw0 + 31);
-      if (active) {
-        const bool edge = (CAUSAL && k0 + BC - 1 > qw0) || (k0 + BC > N);
-        bf16x8 dsb[4];
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          f32x16 S = f32x16{}, dP = f32x16{};
-          const int row = 32 * t2 + perm32(li);
-#pragma unroll
-          for (int kc = 0; kc < D / 16; ++kc) {
-            S = mfma32(tile_read<2 * D>(st + T::OFF_K, row, 2 * kc + h), qf[kc], S);
-            dP = mfma32(tile_read<2 * D>(st + T::OFF_V, row, 2 * kc + h), df[kc], dP);
-          }
-          float dsv[16];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], c, -lse2));
-            if (edge) {
-              const int key = k0 + 32 * t2 + acc_row(r, h);
-              if ((CAUSAL && key > qi) || key >= N) pv = 0.f;
-            }
-            dsv[r] = pv * (dP[r] - Di);
-          }
-          dsb[2 * t2 + 0] = to_bf16x8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
-          dsb[2 * t2 + 1] = to_bf16x8(dsv[8], dsv[9], dsv[10], dsv[11], dsv[12], dsv[13], dsv[14], dsv[15]);
-        }
-#pragma unroll
-        for (int ct = 0; ct < D / 32; ++ct) {
-          const int crow = 32 * ct + perm32(li);
-#pragma unroll
-          for (int kc = 0; kc < BC / 16; ++kc)
-            dq[ct] = mfma32(tile_read<2 * BC>(st + T::OFF_KT, crow, 2 * kc + h), dsb[kc], dq[ct]);
-        }
-      }
-      if (t + 1 < ntiles) store_tile(smem + ((t + 1) & 1) * T::STAGE);
-      if (t + 2 < ntiles) {
-        const int k2 = tile_of(t + 2) * BC;
-        ks.load(Kh, k2, N, tid);
-        vs.load(Vh, k2, N, tid);
-      }
+      if (active(k0)) compute(kc_, vc_, k0);
+      __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
+    };
+    for (int t = 0; t < ntiles; t += 2) {
+      step(t, kb0, vb0, kb1, vb1);
+      if (t + 1 < ntiles) step(t + 1, kb1, vb1, kb0, vb0);
     }
   }
 
@@ -390,7 +448,7 @@ __global__ __launch_bounds__(256, DqTile<D>::MIN_WG) void bwd_dq_kernel(BwdArgs 
     float* dQrow = a.dq + head + (size_t)qi * D;
     const float sc = a.scale;
 #pragma unroll
-    for (int ct = 0; ct < D / 32; ++ct)
+    for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const int col = 32 * ct + 16 * hh + 8 * h;

@@ -50,22 +50,15 @@ __device__ __forceinline__ int swz(int row, int chunk, int nchunk) {
   return chunk ^ (f & (nchunk - 1));
 }
 
-// Swizzle of a natural [rows][D] bf16 tile whose rows are read as MFMA
-// operands with ds_read_b128 in perm32 row order: chunk ^ kswz(row) keeps
-// every 16 consecutive lanes on distinct LDS banks for 128- and 256-byte rows.
+// XOR swizzle of the 16-byte chunks of a natural [rows][D] bf16 LDS tile.
+// The tiles are read two ways: ds_read_b128 of whole rows in perm32 order
+// (MFMA operands that contract over d) and ds_read_b64_tr_b16 of 4-row by
+// 32-byte blocks (operands that contract over the sequence).  Measured on
+// gfx950, chunk ^ tswz(row) keeps both patterns free of bank conflicts for
+// 128- and 256-byte rows.  It depends on row % 16 only.
 template <int D>
-__device__ __forceinline__ int kswz(int row) {
-  if (D == 64) return (row >> 1) & 7;
-  const int b3 = (row >> 3) & 1;
-  return ((row & 7) ^ (b3 << 2)) | (b3 << 3);
-}
-
-// Swizzle of a natural [rows][D] bf16 tile read with ds_read_b64_tr_b16
-// (4 consecutive rows x 32 bytes per 16 lanes): conflict-free for 128- and
-// 256-byte rows.
-template <int D>
-__device__ __forceinline__ int vswz(int row) {
-  return ((((row >> 1) & 1) << 2) | ((row >> 2) & 3) | ((row & 1) << 3)) & (D / 8 - 1);
+__device__ __forceinline__ int tswz(int row) {
+  return (((row & 1) << 3) | (((row >> 1) & 1) << 2) | ((row >> 2) & 3)) & (D / 8 - 1);
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -108,12 +101,6 @@ __device__ __forceinline__ float sum8(bf16x8 v, float acc) {
   a0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one, a0, false);
   a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one, a1, false);
   return a0 + a1;
-}
-
-// 16-byte direct-to-LDS copy (global_load_lds_dwordx4): lane l of the wave
-// writes its 16 bytes at lds + 16*l; lds must be wave-uniform.
-__device__ __forceinline__ void lds_dma16(const void* src, char* lds) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
 
 __device__ __forceinline__ bf16x8 lds_read16(const char* p) {
@@ -275,5 +262,87 @@ __device__ __forceinline__ bf16x8 tile_read(const char* lds, int row, int chunk)
   constexpr int CH = PITCH_BYTES / 16;
   return lds_read16(lds + row * PITCH_BYTES + swz(row, chunk, CH) * 16);
 }
+
+// 16-byte direct-to-LDS copy (global_load_lds_dwordx4): lane l of the wave
+// writes its 16 bytes at lds + 16*l; lds must be wave-uniform.
+__device__ __forceinline__ void lds_dma16(const void* src, char* lds) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
+// Direct-to-LDS copy of ROWS consecutive rows of a [N][D] bf16 matrix into
+// a natural LDS tile swizzled by tswz, by NT threads.  Wave w, round e fills
+// LDS bytes [(e*NW + w) * 1024, +1024), lane l landing at +16*l; that slot
+// holds tile row (e*NW + w) * (1024 / PITCH) + l / CPR, physical chunk
+// l % CPR, i.e. logical chunk (l % CPR) ^ tswz(row).  The per-lane source
+// offsets are the same for every tile.
+template <int ROWS, int D, int NT>
+struct TileCopy {
+  static constexpr int NW = NT / 64;
+  static constexpr int PITCH = 2 * D;
+  static constexpr int CPR = PITCH / 16;
+  static constexpr int ROUNDS = ROWS * PITCH / (NT * 16);
+  static_assert(ROWS * PITCH % (NT * 16) == 0, "tile must be a whole number of rounds");
+  uint32_t off[ROUNDS];  // byte offset of this lane's 16 bytes within the rows
+  int row[ROUNDS];       // tile row of this lane's 16 bytes
+
+  __device__ __forceinline__ void init(int w, int lane) {
+#pragma unroll
+    for (int e = 0; e < ROUNDS; ++e) {
+      row[e] = (e * NW + w) * (1024 / PITCH) + lane / CPR;
+      off[e] = (uint32_t)(row[e] * PITCH + (((lane % CPR) ^ tswz<D>(row[e])) << 4));
+    }
+  }
+  // rows [row0, row0 + ROWS) of src; rows past N re-read row N-1 (finite
+  // data that the callers mask)
+  __device__ __forceinline__ void issue(char* lds_tile, const __bf16* src, int row0, int N, int w) const {
+    const char* base = reinterpret_cast<const char*>(src + (size_t)row0 * D);
+    if (row0 + ROWS <= N) {
+#pragma unroll
+      for (int e = 0; e < ROUNDS; ++e) lds_dma16(base + off[e], lds_tile + (e * NW + w) * 1024);
+    } else {
+      const uint32_t last = (uint32_t)((N - 1 - row0) * PITCH);  // byte offset of row N-1
+#pragma unroll
+      for (int e = 0; e < ROUNDS; ++e) {
+        const uint32_t o = (row0 + row[e] < N) ? off[e] : last + (off[e] - (uint32_t)(row[e] * PITCH));
+        lds_dma16(base + o, lds_tile + (e * NW + w) * 1024);
+      }
+    }
+  }
+};
+
+// Per-lane byte offsets of the MFMA operands in a tswz-swizzled natural tile.
+// rows(): A operand rows perm32(li) (+32*t), 16-byte chunk 2kc + h: one
+//   ds_read_b128 per k-step of a product that contracts over d.
+// tr(): the A operand of a product that contracts over the tile's rows: for
+//   read r of a 16-row k-step and 32-column group ct, lane l addresses tile
+//   row 8h + 4r + (l%16)/4 (+16*kc) and columns 32ct + perm32(16*((l/16)%2) +
+//   4*(l%4)) .. +3; two ds_read_b64_tr_b16 then give lane l column
+//   32ct + perm32(l%32), rows 16kc + 8h .. +7.
+template <int D>
+struct TileOffsets {
+  static constexpr int PITCH = 2 * D;
+  int rows[D / 16];
+  int tr[D / 32][2];
+  __device__ __forceinline__ void init(int lane) {
+    const int h = lane >> 5, li = lane & 31;
+    const int rr = perm32(li);
+#pragma unroll
+    for (int kc = 0; kc < D / 16; ++kc) rows[kc] = rr * PITCH + (((2 * kc + h) ^ tswz<D>(rr)) << 4);
+    const int trow = 8 * h + ((lane & 15) >> 2);
+    const int tcl = 2 * ((lane >> 4) & 1) + (lane & 1);
+#pragma unroll
+    for (int ct = 0; ct < D / 32; ++ct)
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int row = trow + 4 * r;
+        tr[ct][r] = row * PITCH + (((4 * ct + tcl) ^ tswz<D>(row)) << 4) + ((lane >> 1) & 1) * 8;
+      }
+  }
+  // A operand (transposed), rows 16*kc .. +15 of the tile, columns group ct
+  __device__ __forceinline__ bf16x8 read_tr(const char* tile, int kc, int ct) const {
+    const auto* base = (const __attribute__((address_space(3))) char*)(tile + 16 * kc * PITCH);
+    return cat8(lds_read_tr8(base + tr[ct][0]), lds_read_tr8(base + tr[ct][1]));
+  }
+};
 
 }  // namespace fa

@@ -65,7 +65,6 @@ struct FwdTile {
   static constexpr int PITCH = 2 * D;    // bytes per K or V row in LDS
   static constexpr int T_BYTES = BC * PITCH;
   static constexpr int STAGE = 2 * T_BYTES;  // K tile then V tile
-  static constexpr int ROUNDS = T_BYTES / (NT * 16);  // 16-byte copies per thread per tile
   static constexpr int LIST_CAP = 1024;  // mask blocks listed per pass
   // Two workgroups per CU (two waves per SIMD): one wave's softmax overlaps
   // the other's products.  At d=64 a wave also keeps the scores of the next
@@ -73,46 +72,6 @@ struct FwdTile {
   // wave has at this occupancy.
   static constexpr int MIN_WG = 2;
   static constexpr bool PIPE = (D == 64);
-};
-
-// Direct-to-LDS copy of one BC-row tile of a [N][D] bf16 matrix into a
-// natural, swizzled LDS tile.  Wave w, round e fills LDS bytes
-// [(e*NW + w) * 1024, +1024), lane l landing at +16*l; that slot holds tile
-// row (e*NW + w) * (1024 / PITCH) + l / CPR, physical chunk l % CPR, i.e.
-// logical chunk (l % CPR) ^ swizzle(row).  The per-lane source offsets are
-// fixed for every tile, so a copy costs one instruction per round.
-template <int D, bool VTILE>
-struct TileCopy {
-  using T = FwdTile<D>;
-  static constexpr int CPR = T::PITCH / 16;
-  uint32_t off[T::ROUNDS];  // byte offset of this lane's 16 bytes within the tile
-  int row[T::ROUNDS];       // tile row of this lane's 16 bytes
-
-  __device__ __forceinline__ void init(int w, int lane) {
-#pragma unroll
-    for (int e = 0; e < T::ROUNDS; ++e) {
-      row[e] = (e * T::NW + w) * (1024 / T::PITCH) + lane / CPR;
-      const int logical = (lane % CPR) ^ (VTILE ? vswz<D>(row[e]) : kswz<D>(row[e]));
-      off[e] = (uint32_t)(row[e] * (2 * D) + logical * 16);
-    }
-  }
-  // rows [row0, row0 + BC) of src; rows past N re-read row N-1 (finite data
-  // that the mask zeroes)
-  __device__ __forceinline__ void issue(char* lds_tile, const __bf16* src, int row0, int N, int w) const {
-    const char* base = reinterpret_cast<const char*>(src + (size_t)row0 * D);
-    if (row0 + T::BC <= N) {
-#pragma unroll
-      for (int e = 0; e < T::ROUNDS; ++e)
-        lds_dma16(base + off[e], lds_tile + (e * T::NW + w) * 1024);
-    } else {
-      const uint32_t over = (uint32_t)((N - 1 - row0) * (2 * D));  // byte offset of row N-1
-#pragma unroll
-      for (int e = 0; e < T::ROUNDS; ++e) {
-        const uint32_t o = (row0 + row[e] < N) ? off[e] : over + (off[e] - (uint32_t)(row[e] * (2 * D)));
-        lds_dma16(base + o, lds_tile + (e * T::NW + w) * 1024);
-      }
-    }
-  }
 };
 
 template <int D, bool CAUSAL, bool MASK>
@@ -159,25 +118,9 @@ __global__ __launch_bounds__(256, FwdTile<D>::MIN_WG) void fwd_bf16_kernel(FwdAr
     qf[kc] = __builtin_bit_cast(bf16x8, x);
   }
 
-  // Per-lane LDS offsets, fixed for every tile.
-  // K operand (A of S^T): row perm32(li) (+32 for the second key half), chunk 2kc+h.
-  const int krow = perm32(li);
-  int koff[NKC];
-#pragma unroll
-  for (int kc = 0; kc < NKC; ++kc) koff[kc] = krow * PITCH + (((2 * kc + h) ^ kswz<D>(krow)) << 4);
-  // V^T operand (A of O^T) by transposed reads: for read r of k-step kc and
-  // O^T tile ct, lane l addresses key row 16kc + 8h + 4r + (l%16)/4 and
-  // columns 32ct + perm32(16*((l/16)%2) + 4*(l%4)) .. +3.
-  const int vrow = 8 * h + ((lane & 15) >> 2);
-  const int vcl = 2 * ((lane >> 4) & 1) + (lane & 1);  // 16-byte chunk within a 32-column group
-  int voff[NCT][2];
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int row = vrow + 4 * r;
-      voff[ct][r] = row * PITCH + (((4 * ct + vcl) ^ vswz<D>(row)) << 4) + ((lane >> 1) & 1) * 8;
-    }
+  // Per-lane LDS offsets of the K (rows) and V^T (transposed) operands.
+  TileOffsets<D> toff;
+  toff.init(lane);
 
   f32x16 o[NCT];
 #pragma unroll
@@ -187,8 +130,8 @@ __global__ __launch_bounds__(256, FwdTile<D>::MIN_WG) void fwd_bf16_kernel(FwdAr
 
   const int ntiles_all = (N + BC - 1) / BC;
   const float c = a.c;
-  TileCopy<D, false> kcopy;
-  TileCopy<D, true> vcopy;
+  TileCopy<BC, D, NT> kcopy;
+  TileCopy<BC, D, NT> vcopy;
   kcopy.init(w, lane);
   vcopy.init(w, lane);
 
@@ -197,8 +140,8 @@ __global__ __launch_bounds__(256, FwdTile<D>::MIN_WG) void fwd_bf16_kernel(FwdAr
     bf16x8 ka0[NKC], ka1[NKC];
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) {
-      ka0[kc] = lds_read16(kt + koff[kc]);
-      ka1[kc] = lds_read16(kt + koff[kc] + 32 * PITCH);
+      ka0[kc] = lds_read16(kt + toff.rows[kc]);
+      ka1[kc] = lds_read16(kt + toff.rows[kc] + 32 * PITCH);
     }
     s0 = f32x16{};
     s1 = f32x16{};
@@ -257,8 +200,8 @@ __global__ __launch_bounds__(256, FwdTile<D>::MIN_WG) void fwd_bf16_kernel(FwdAr
       bf16x8 ka0[NKC], ka1[NKC];
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) {
-        ka0[kc] = lds_read16(knext + koff[kc]);
-        ka1[kc] = lds_read16(knext + koff[kc] + 32 * PITCH);
+        ka0[kc] = lds_read16(knext + toff.rows[kc]);
+        ka1[kc] = lds_read16(knext + toff.rows[kc] + 32 * PITCH);
       }
       n0 = f32x16{};
       n1 = f32x16{};
@@ -304,9 +247,7 @@ __global__ __launch_bounds__(256, FwdTile<D>::MIN_WG) void fwd_bf16_kernel(FwdAr
     for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
       for (int kc = 0; kc < BC / 16; ++kc) {
-        const auto* base = (const __attribute__((address_space(3))) char*)(vt + 16 * kc * PITCH);
-        const bf16x8 av = cat8(lds_read_tr8(base + voff[ct][0]), lds_read_tr8(base + voff[ct][1]));
-        o[ct] = mfma32(av, pb[kc], o[ct]);
+        o[ct] = mfma32(toff.read_tr(vt, kc, ct), pb[kc], o[ct]);
       }
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 2);
 #pragma unroll
