@@ -19,6 +19,8 @@
 //             instead of accumulating dQ with atomics)
 #pragma once
 
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_fwd.h"
 #include "fa_sched.h"
@@ -82,7 +84,11 @@ struct DkdvTile {
   static constexpr int PITCH = 2 * D;
   static constexpr int T_BYTES = BQ * PITCH;
   static constexpr int LIST_CAP = 1024;
-  static constexpr int MIN_WG = (D == 64) ? 2 : 1;
+  // d=128 pipelines the two 32-query sub-blocks of a tile, which needs the
+  // registers of one wave per SIMD; d=64 runs them one after the other with
+  // two waves per SIMD (measured faster at that size).
+  static constexpr bool PIPE = (D == 128);
+  static constexpr int MIN_WG = PIPE ? 1 : 2;
 };
 
 template <int D, bool CAUSAL, bool MASK>
@@ -152,7 +158,119 @@ __global__ __launch_bounds__(256, DkdvTile<D>::MIN_WG) void bwd_dkdv_kernel(BwdA
     else if (w == 1) eb[lane] = x;
   };
 
-  auto compute = [&] __device__ (const char* qt, const char* dt, const float* lt, const float* et, int q0) {
+  // S = Q K^T and dP = dO V^T for the 32-query sub-block at `qs`/`ds`.
+  auto products = [&] __device__ (const char* qs, const char* ds, f32x16& S, f32x16& dP) {
+    bf16x8 aq[NKC], ad[NKC];
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      aq[kc] = lds_read16(qs + toff.rows[kc]);
+      ad[kc] = lds_read16(ds + toff.rows[kc]);
+    }
+    S = f32x16{};
+    dP = f32x16{};
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      S = mfma32(aq[kc], kf[kc], S);
+      dP = mfma32(ad[kc], vf[kc], dP);
+    }
+  };
+  // P = 2^(S*c - lse*log2 e) and dS = P o (dP - D) of sub-block sb, as bf16
+  // B operands (queries of the lane: 32sb + 16*hf + 8h + e).
+  auto grads = [&] __device__ (auto edge_c, const f32x16& S, const f32x16& dP, const float* lt,
+                               const float* et, int sb, int q0, bf16x8* pb, bf16x8* sbv) {
+    constexpr bool EDGE = decltype(edge_c)::value;
+    const int qs0 = q0 + 32 * sb;
+    float p[16], dsv[16];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const f32x4 l0 = *reinterpret_cast<const f32x4*>(lt + 32 * sb + 16 * hf + 8 * h);
+      const f32x4 l1 = *reinterpret_cast<const f32x4*>(lt + 32 * sb + 16 * hf + 8 * h + 4);
+      const f32x4 e0 = *reinterpret_cast<const f32x4*>(et + 32 * sb + 16 * hf + 8 * h);
+      const f32x4 e1 = *reinterpret_cast<const f32x4*>(et + 32 * sb + 16 * hf + 8 * h + 4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = 8 * hf + e;
+        const float lv = e < 4 ? l0[e] : l1[e - 4];
+        const float dvv = e < 4 ? e0[e] : e1[e - 4];
+        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], c, -lv));
+        if (EDGE) {
+          const int qq = qs0 + acc_row(r, h);
+          if ((CAUSAL && kj > qq) || qq >= N) pv = 0.f;
+        }
+        p[r] = pv;
+        dsv[r] = pv * (dP[r] - dvv);
+      }
+    }
+    pb[0] = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+    pb[1] = to_bf16x8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
+    sbv[0] = to_bf16x8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
+    sbv[1] = to_bf16x8(dsv[8], dsv[9], dsv[10], dsv[11], dsv[12], dsv[13], dsv[14], dsv[15]);
+  };
+  // dV^T += dO^T P and dK^T += Q^T dS for one sub-block (scale at the end)
+  auto accumulate = [&] __device__ (const char* qs, const char* ds, const bf16x8* pb, const bf16x8* sbv) {
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      dv[ct] = mfma32(toff.read_tr(ds, 0, ct), pb[0], dv[ct]);
+      dv[ct] = mfma32(toff.read_tr(ds, 1, ct), pb[1], dv[ct]);
+      dk[ct] = mfma32(toff.read_tr(qs, 0, ct), sbv[0], dk[ct]);
+      dk[ct] = mfma32(toff.read_tr(qs, 1, ct), sbv[1], dk[ct]);
+    }
+  };
+
+  // One 64-query tile as a software pipeline over its two 32-query
+  // sub-blocks, in one scheduling region: products(0); products(1) with
+  // grads(0) on the VALU; accumulate(0) with grads(1); accumulate(1).
+  auto compute = [&] __device__ (auto edge_c, const char* qt, const char* dt, const float* lt,
+                                 const float* et, int q0) {
+    const char* qs1 = qt + 32 * PITCH;
+    const char* ds1 = dt + 32 * PITCH;
+    f32x16 S0, dP0, S1, dP1;
+    bf16x8 pb0[2], sv0[2], pb1[2], sv1[2];
+    // phase A: products(0), operand reads three k-steps ahead
+    products(qt, dt, S0, dP0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 3);
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 3);
+      if (kc + 3 < NKC) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 3);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // phase B: products(1) on the matrix pipe, grads(0) on the VALU
+    products(qs1, ds1, S1, dP1);
+    grads(edge_c, S0, dP0, lt, et, 0, q0, pb0, sv0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 4);
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 4);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, 40 / NKC, 4);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 4);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, 40 / NKC, 4);
+      if (kc + 3 < NKC) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 4);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // phase C: accumulate(0) on the matrix pipe, grads(1) on the VALU
+    accumulate(qt, dt, pb0, sv0);
+    grads(edge_c, S1, dP1, lt, et, 1, q0, pb1, sv1);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 5);
+#pragma unroll
+    for (int m = 0; m < 4 * NCT; ++m) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 5);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, 80 / (4 * NCT), 5);
+      if (m + 2 < 4 * NCT) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 5);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // phase D: accumulate(1)
+    accumulate(qs1, ds1, pb1, sv1);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 6);
+#pragma unroll
+    for (int m = 0; m < 4 * NCT; ++m) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 6);
+      if (m + 2 < 4 * NCT) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 6);
+    }
+  };
+
+  // Sub-blocks one after the other (d=64, two waves per SIMD).
+  auto compute_seq = [&] __device__ (const char* qt, const char* dt, const float* lt, const float* et, int q0) {
 #pragma unroll
     for (int sb = 0; sb < BQ / 32; ++sb) {
       const int qs0 = q0 + 32 * sb;
@@ -256,7 +374,18 @@ __global__ __launch_bounds__(256, DkdvTile<D>::MIN_WG) void bwd_dkdv_kernel(BwdA
         cp.issue(dn, dOh, q1, N, w);
         nv = load_vec(q1);
       }
-      if (kw0 < N) compute(qc, dc, lc, ec, tile_of(t) * BQ);
+      const int q0 = tile_of(t) * BQ;
+      if constexpr (T::PIPE) {
+        // masking only where the tile crosses the diagonal or the sequence end
+        if (kw0 < N && !(CAUSAL && q0 + BQ - 1 < kw0)) {
+          if ((CAUSAL && q0 < kw0 + 31) || (q0 + BQ > N))
+            compute(std::true_type{}, qc, dc, lc, ec, q0);
+          else
+            compute(std::false_type{}, qc, dc, lc, ec, q0);
+        }
+      } else {
+        if (kw0 < N) compute_seq(qc, dc, lc, ec, q0);
+      }
       if (t + 1 < ntiles) store_vec(ln, en, nv);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
