@@ -136,6 +136,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long_causal_16k", choices=sorted(BENCH_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only copy MIB mebibytes device-to-device three times (the known-size "
+                         "reference for the FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -144,6 +147,15 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        x = torch.empty(args.copy_calibration << 20, dtype=torch.uint8, device="cuda:0")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": x.numel(), "copies": 3}), flush=True)
+        return
 
     import exact_io_aware_18_amd as fa
     from exact_io_aware_18_amd.inputs import WORKLOADS, default_scale, make_blockmask, make_qkvdo
