@@ -74,14 +74,23 @@ void launch_fwd_t(const fa::FwdArgs& a, int grid, hipStream_t s) {
   hipLaunchKernelGGL((fa::fwd_bf16_kernel<D, CAUSAL, MASK>), dim3(grid), dim3(256), 0, s, a);
 }
 
+template <int D, bool CAUSAL>
+void launch_fwd_pp(fa::FwdArgs a, int BH, hipStream_t s) {
+  a.nqt = (a.N + fa::FwdPPTile<D>::BR - 1) / fa::FwdPPTile<D>::BR;
+  a.total = BH * a.nqt;
+  hipLaunchKernelGGL((fa::fwd_pp_kernel<D, CAUSAL>), dim3(a.total), dim3(fa::FwdPPTile<D>::NT), 0, s, a);
+}
+
+// Dense and causal use the ping-pong kernel (256 query rows per workgroup);
+// a block mask needs 128-row workgroups (one mask row each).
 template <int D>
-void launch_fwd_d(const fa::FwdArgs& a, int grid, bool causal, bool mask, hipStream_t s) {
-  if (causal) {
-    if (mask) launch_fwd_t<D, true, true>(a, grid, s);
-    else launch_fwd_t<D, true, false>(a, grid, s);
+void launch_fwd_d(const fa::FwdArgs& a, int BH, bool causal, bool mask, hipStream_t s) {
+  if (mask) {
+    if (causal) launch_fwd_t<D, true, true>(a, a.total, s);
+    else launch_fwd_t<D, false, true>(a, a.total, s);
   } else {
-    if (mask) launch_fwd_t<D, false, true>(a, grid, s);
-    else launch_fwd_t<D, false, false>(a, grid, s);
+    if (causal) launch_fwd_pp<D, true>(a, BH, s);
+    else launch_fwd_pp<D, false>(a, BH, s);
   }
 }
 
@@ -267,8 +276,8 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   a.negate_q = scale < 0.f;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  if (d == 64) launch_fwd_d<64>(a, a.total, causal, blockmask != nullptr, s);
-  else launch_fwd_d<128>(a, a.total, causal, blockmask != nullptr, s);
+  if (d == 64) launch_fwd_d<64>(a, B * H, causal, blockmask != nullptr, s);
+  else launch_fwd_d<128>(a, B * H, causal, blockmask != nullptr, s);
   return launched();
 }
 

@@ -337,4 +337,226 @@ __global__ __launch_bounds__(256, FwdTile<D>::MIN_WG) void fwd_bf16_kernel(FwdAr
   }
 }
 
+// ---- ping-pong forward (dense and causal) -----------------------------------
+// One workgroup of eight waves owns 256 query rows: waves 0-3 (group A) the
+// first 128, waves 4-7 (group B) the next 128; waves w and w+4 share a SIMD.
+// Per key tile a wave does a matrix phase M (O^T += V^T P^T of the previous
+// tile, then S^T = K Q^T of this tile) and a vector phase V (softmax of this
+// tile's scores).  Barriers hold the two groups half a tile apart, so on every
+// SIMD one wave's products run while the other wave's softmax runs:
+//   round r, phase 1:  A: M(r)      B: V(r-1)
+//   round r, phase 2:  A: V(r)      B: M(r)
+// Round r reads K(r) and V(r-1); K(r+1) and V(r) are copied meanwhile into
+// the buffers round r-1 finished with.
+template <int D>
+struct FwdPPTile {
+  static constexpr int NW = 8;
+  static constexpr int NT = 64 * NW;
+  static constexpr int BR = 256;   // query rows per workgroup
+  static constexpr int BC = 64;    // keys per tile
+  static constexpr int PITCH = 2 * D;
+  static constexpr int T_BYTES = BC * PITCH;
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
+  using T = FwdPPTile<D>;
+  constexpr int BC = T::BC, BR = T::BR, NT = T::NT, PITCH = T::PITCH;
+  constexpr int NKC = D / 16, NCT = D / 32;
+  __shared__ __attribute__((aligned(1024))) char kb0[T::T_BYTES];
+  __shared__ __attribute__((aligned(1024))) char kb1[T::T_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vb0[T::T_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vb1[T::T_BYTES];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool grpA = w < 4;
+  const int h = lane >> 5, li = lane & 31;
+
+  const int g = xcd_remap(blockIdx.x, a.total);
+  const int bh = g / a.nqt;
+  int qt = g - bh * a.nqt;
+  if (CAUSAL) qt = a.nqt - 1 - qt;  // longest rows first
+  const int N = a.N;
+  const size_t head = (size_t)bh * N * D;
+  const __bf16* Qh = a.q + head;
+  const __bf16* Kh = a.k + head;
+  const __bf16* Vh = a.v + head;
+  const int q0 = qt * BR;
+  const int qw0 = q0 + 32 * w;  // first query of this wave
+  const int qi = qw0 + li;
+
+  bf16x8 qf[NKC];
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc) {
+    u32x4 x = u32x4{0u, 0u, 0u, 0u};
+    if (qi < N) x = gload16(Qh + (size_t)qi * D + 16 * kc + 8 * h);
+    if (a.negate_q) x ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+    qf[kc] = __builtin_bit_cast(bf16x8, x);
+  }
+  TileOffsets<D> toff;
+  toff.init(lane);
+  TileCopy<BC, D, NT> cp;
+  cp.init(w, lane);
+
+  f32x16 o[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) o[ct] = f32x16{};
+  float Mref = -INFINITY, L = 0.f;
+  const float c = a.c;
+  const int kend = CAUSAL ? min(N, q0 + BR) : N;
+  const int ntiles = (kend + BC - 1) / BC;
+  // tiles this wave has visible keys in: [0, wtiles)
+  const int wtiles = (qw0 >= N) ? 0 : (CAUSAL ? min(ntiles, (qw0 + 31) / BC + 1) : ntiles);
+
+  f32x16 s0, s1;  // scores of the current tile
+  bf16x8 pb[4];   // P of the previous tile (bf16)
+
+  // matrix phase of round r: O^T += V^T P^T for tile r-1, then S^T of tile r
+  auto mphase = [&] __device__ (int r, const char* kt, const char* vprev) {
+    if (r >= 1 && r - 1 < wtiles) {
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int kc = 0; kc < BC / 16; ++kc) o[ct] = mfma32(toff.read_tr(vprev, kc, ct), pb[kc], o[ct]);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 13);
+#pragma unroll
+      for (int m = 0; m < NCT * BC / 16; ++m) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 13);
+        if (m + 2 < NCT * BC / 16) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 13);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (r < wtiles) {
+      bf16x8 ka0[NKC], ka1[NKC];
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        ka0[kc] = lds_read16(kt + toff.rows[kc]);
+        ka1[kc] = lds_read16(kt + toff.rows[kc] + 32 * PITCH);
+      }
+      s0 = f32x16{};
+      s1 = f32x16{};
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        s0 = mfma32(ka0[kc], qf[kc], s0);
+        s1 = mfma32(ka1[kc], qf[kc], s1);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 14);
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 14);
+        if (kc + 2 < NKC) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 14);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // vector phase: softmax of the scores of tile r into pb
+  auto vphase = [&] __device__ (int r) {
+    if (r < 0 || r >= wtiles) return;
+    const int k0 = r * BC;
+    const bool edge = (CAUSAL && k0 + BC - 1 > qw0) || (k0 + BC > N);
+    if (edge) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key0 = k0 + acc_row(e, h), key1 = key0 + 32;
+        if ((CAUSAL && key0 > qi) || key0 >= N) s0[e] = -INFINITY;
+        if ((CAUSAL && key1 > qi) || key1 >= N) s1[e] = -INFINITY;
+      }
+    }
+    float m0 = fmaxf(s0[0], s0[1]), m1 = fmaxf(s1[0], s1[1]);
+#pragma unroll
+    for (int e = 2; e < 16; e += 2) {
+      m0 = fmaxf(fmaxf(m0, s0[e]), s0[e + 1]);
+      m1 = fmaxf(fmaxf(m1, s1[e]), s1[e + 1]);
+    }
+    const float mx = xhalf_max(fmaxf(m0, m1));
+    const float mt = (mx == -INFINITY) ? -INFINITY : mx * c;
+    const bool need = mt > Mref + kLazyTau;
+    if (wave_any(need)) {
+      const float Mn = need ? mt : Mref;
+      const float alpha = need ? __builtin_amdgcn_exp2f(Mref - Mn) : 1.f;
+      L *= alpha;
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) o[ct] *= alpha;
+      Mref = Mn;
+    }
+    const float mb = (Mref == -INFINITY) ? 0.f : Mref;
+    float lsum[4];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      float p0[8], p1[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p0[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[8 * hh + e], c, -mb));
+        p1[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[8 * hh + e], c, -mb));
+      }
+      pb[hh] = to_bf16x8(p0[0], p0[1], p0[2], p0[3], p0[4], p0[5], p0[6], p0[7]);
+      pb[2 + hh] = to_bf16x8(p1[0], p1[1], p1[2], p1[3], p1[4], p1[5], p1[6], p1[7]);
+      lsum[hh] = ((p0[0] + p0[1]) + (p0[2] + p0[3])) + ((p0[4] + p0[5]) + (p0[6] + p0[7]));
+      lsum[2 + hh] = ((p1[0] + p1[1]) + (p1[2] + p1[3])) + ((p1[4] + p1[5]) + (p1[6] + p1[7]));
+    }
+    L += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+  };
+
+  // prologue: K(0) into kb0
+  if (ntiles > 0) cp.issue(kb0, Kh, 0, N, w);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  // round r (r = 0 .. ntiles): K(r) in kb[r&1], V(r-1) in vb[(r-1)&1].
+  // Each group runs its own loop (the phase order differs); both execute the
+  // same two barriers per round.
+  auto copies = [&] __device__ (int r, char* knext, char* vcur) {
+    if (r + 1 < ntiles) cp.issue(knext, Kh, (r + 1) * BC, N, w);
+    if (r < ntiles) cp.issue(vcur, Vh, r * BC, N, w);
+  };
+  if (grpA) {
+    auto roundA = [&] __device__ (int r, const char* kcur, char* knext, const char* vprev, char* vcur) {
+      copies(r, knext, vcur);
+      mphase(r, kcur, vprev);
+      __syncthreads();
+      vphase(r);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    };
+    for (int r = 0; r <= ntiles; r += 2) {
+      roundA(r, kb0, kb1, vb1, vb0);
+      if (r + 1 <= ntiles) roundA(r + 1, kb1, kb0, vb0, vb1);
+    }
+  } else {
+    auto roundB = [&] __device__ (int r, const char* kcur, char* knext, const char* vprev, char* vcur) {
+      copies(r, knext, vcur);
+      vphase(r - 1);
+      __syncthreads();
+      mphase(r, kcur, vprev);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    };
+    for (int r = 0; r <= ntiles; r += 2) {
+      roundB(r, kb0, kb1, vb1, vb0);
+      if (r + 1 <= ntiles) roundB(r + 1, kb1, kb0, vb0, vb1);
+    }
+  }
+
+  const float Lt = xhalf_sum(L);
+  if (qi < N) {
+    const bool empty = !(Lt > 0.f);
+    const float inv = empty ? 0.f : 1.f / Lt;
+    __bf16* Orow = a.o + head + (size_t)qi * D;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int col = 32 * ct + 16 * hh + 8 * h;
+        const f32x16& x = o[ct];
+        const int r0 = 8 * hh;
+        bf16x8 v = to_bf16x8(x[r0] * inv, x[r0 + 1] * inv, x[r0 + 2] * inv, x[r0 + 3] * inv,
+                             x[r0 + 4] * inv, x[r0 + 5] * inv, x[r0 + 6] * inv, x[r0 + 7] * inv);
+        *reinterpret_cast<bf16x8*>(Orow + col) = v;
+      }
+    if (h == 0) a.lse[(size_t)bh * N + qi] = empty ? -INFINITY : (Mref + __log2f(Lt)) * kLn2;
+  }
+}
+
 }  // namespace fa
