@@ -87,6 +87,69 @@ def load_traffic(kernel_key: str):
 
 
 CPU_SAMPLE_HEADS = 4
+COLD_FLUSH_BYTES = 512 << 20  # written between cold steps: twice the 256 MB last-level cache
+
+
+def percentiles(xs):
+    """p10 / median / p90 of a list of per-step durations (nearest rank)."""
+    ys = sorted(xs)
+    pick = lambda f: ys[min(len(ys) - 1, max(0, int(round(f * (len(ys) - 1)))))]
+    return {"p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9)}
+
+
+class ClockSampler:
+    """Polls the GPU's current shader clock (the DPM level marked '*' in the
+    kernel driver's pp_dpm_sclk file) from a background thread while the timed
+    steps run.  Reports None where the file is not readable."""
+
+    def __init__(self, period_s=0.005):
+        import glob
+
+        self.files = [f for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+                      if os.access(f, os.R_OK)]
+        self.period = period_s
+        self.samples = []
+        self._stop = False
+        self._thread = None
+
+    def _read(self):
+        for f in self.files:
+            try:
+                with open(f) as fh:
+                    for line in fh:
+                        if line.rstrip().endswith("*"):
+                            mhz = line.split(":")[1].strip().split()[0].lower().replace("mhz", "")
+                            return float(mhz)
+            except (OSError, ValueError, IndexError):
+                continue
+        return None
+
+    def _run(self):
+        while not self._stop:
+            v = self._read()
+            if v is not None:
+                self.samples.append(v)
+            time.sleep(self.period)
+
+    def __enter__(self):
+        import threading
+
+        if self.files:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop = True
+        if self._thread is not None:
+            self._thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        ys = sorted(self.samples)
+        return {"median_mhz": ys[len(ys) // 2], "min_mhz": ys[0], "max_mhz": ys[-1], "samples": len(ys),
+                "source": "pp_dpm_sclk"}
 
 
 def cpu_baseline(sub_names):
@@ -136,6 +199,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long_causal_16k", choices=sorted(BENCH_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-steps", type=int, default=5,
+                    help="extra steps, each after writing %d MiB of scratch (outside the timed "
+                         "region), so that no input is cache-resident; reported per kernel as "
+                         "cold_ms" % (COLD_FLUSH_BYTES >> 20))
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy MIB mebibytes device-to-device three times (the known-size "
                          "reference for the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -217,21 +284,38 @@ def main():
     nev = len(subs) * nk + 1
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    with ClockSampler() as clk:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(evs[i])
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    # cold regime: the inputs are evicted from every cache before each step
+    cold = []
+    if args.cold_steps > 0:
+        flush = torch.empty(COLD_FLUSH_BYTES, dtype=torch.uint8, device=dev)
+        for i in range(args.cold_steps):
+            flush.fill_(i & 0xFF)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(nev)]
+            step(ev)
+            cold.append(ev)
+        torch.cuda.synchronize()
+        del flush
 
     kinds = ["fwd", "bwd_pre", "bwd_dkdv", "bwd_dq"]
     kernels = {}
     for si, s in enumerate(subs):
         for j, kind in enumerate(kinds):
             a = si * nk + j
-            ms = sum(evs[i][a].elapsed_time(evs[i][a + 1]) for i in range(args.steps)) / args.steps
+            per_step = [evs[i][a].elapsed_time(evs[i][a + 1]) for i in range(args.steps)]
+            ms = sum(per_step) / args.steps
             key = f"{kind}_d{s['d']}"
             kernels[key] = {"ms": ms}
+            kernels[key].update({f"ms_{k_}": v_ for k_, v_ in percentiles(per_step).items()})
+            if cold:
+                kernels[key]["cold_ms"] = sorted(ev[a].elapsed_time(ev[a + 1]) for ev in cold)[len(cold) // 2]
             d, p, rows = s["d"], s["pairs"], s["B"] * s["H"] * s["N"]
             if kind == "fwd":
                 kernels[key]["flops"] = 4.0 * d * p
@@ -286,6 +370,10 @@ def main():
         "kernels": {k_: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v_.items()}
                     for k_, v_ in kernels.items()},
         "roofline": roofline,
+        "timing": "warm: back-to-back steps, per-kernel mean (ms) and p10/p50/p90 over the timed "
+                  "steps from HIP events on the launch stream; cold: median over cold_steps steps, "
+                  "each after writing %d MiB of scratch" % (COLD_FLUSH_BYTES >> 20),
+        "sclk": clk.summary(),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline([s["name"] for s in subs])
