@@ -4,8 +4,11 @@ TEST INFRASTRUCTURE ONLY: imported by tests/, by __graft_entry__.smoke() and by
 bench.py's CPU-baseline leg.  The library never imports it, and it imports
 nothing from the library.
 
-Functions and the passages they follow are documented in oracle/attention.py.
-Every function here is pinned by tests/test_oracle_pins.py against closed
+Functions and the passages they follow are documented in oracle/attention.py
+(attention) and oracle/dropout.py (dropout on the attention probabilities,
+with its counter-based generator).
+Every function here is pinned by tests/test_oracle_pins.py and
+tests/test_oracle_dropout_pins.py against closed
 forms, brute force, finite differences and an independent library
 implementation; none is "parity unpinned".
 """
@@ -17,4 +20,11 @@ from .attention import (  # noqa: F401
     attention_dq_rows,
     attention_fwd,
     attention_fwd_rows,
+)
+from .dropout import (  # noqa: F401
+    attention_bwd_dropout,
+    attention_fwd_dropout,
+    drop_threshold,
+    keep_mask,
+    philox4x32_10,
 )
