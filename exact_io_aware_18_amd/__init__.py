@@ -5,10 +5,12 @@ kernels behind the C ABI declared in include/fa.h.  PyTorch provides device
 memory and the current stream.  If the shared library is missing, every call
 raises; there is no fallback implementation.
 
-Low level: fa_fwd, fa_bwd, fa_fwd_f32, fa_bwd_f32, fa_bwd_workspace_bytes,
-fa_strerror and fa_version take the C arguments as they are (pointers as
-integers).  High level: fwd, bwd, fwd_f32 and bwd_f32 take torch tensors,
-allocate the outputs and raise FAError on a nonzero status.
+Low level: one function per exported symbol (fa_fwd, fa_bwd, the three
+backward stages, fa_fwd_dropout, fa_bwd_dropout, fa_fwd_f32, fa_bwd_f32,
+fa_bwd_workspace_bytes, fa_strerror, fa_version) takes the C arguments as they
+are (pointers as integers).  High level: fwd, bwd, bwd_stages, fwd_dropout,
+bwd_dropout, fwd_f32 and bwd_f32 take torch tensors, allocate the outputs and
+raise FAError on a nonzero status.
 """
 from __future__ import annotations
 
@@ -22,10 +24,11 @@ FA_OK = 0
 STATUS_NAMES = {
     0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_SHAPE", -3: "FA_ERR_HEADDIM",
     -4: "FA_ERR_ALIGN", -5: "FA_ERR_ALIAS", -6: "FA_ERR_WORKSPACE", -7: "FA_ERR_FLAG",
-    -8: "FA_ERR_LAUNCH", -9: "FA_ERR_UNSUPPORTED", -10: "FA_ERR_SCALE",
+    -8: "FA_ERR_LAUNCH", -9: "FA_ERR_UNSUPPORTED", -10: "FA_ERR_SCALE", -11: "FA_ERR_DROPOUT",
 }
 EXPORTED = ("fa_fwd", "fa_bwd", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq",
-            "fa_bwd_workspace_bytes", "fa_fwd_f32", "fa_bwd_f32", "fa_strerror", "fa_version")
+            "fa_fwd_dropout", "fa_bwd_dropout", "fa_bwd_workspace_bytes", "fa_fwd_f32",
+            "fa_bwd_f32", "fa_strerror", "fa_version")
 
 _lib = None
 
@@ -44,6 +47,7 @@ def lib() -> ctypes.CDLL:
             raise ImportError(f"{LIB_PATH} is missing; build it with exact_io_aware_18_amd.build.build()")
         L = ctypes.CDLL(LIB_PATH)
         P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        U64 = ctypes.c_ulonglong
         L.fa_fwd.argtypes = [P, P, P, P, P, I, I, I, I, F, I, P, P]
         L.fa_fwd.restype = I
         L.fa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, Z, P]
@@ -54,6 +58,10 @@ def lib() -> ctypes.CDLL:
         L.fa_bwd_dkdv.restype = I
         L.fa_bwd_dq.argtypes = [P, P, P, P, P, P, I, I, I, I, F, I, P, P, Z, P]
         L.fa_bwd_dq.restype = I
+        L.fa_fwd_dropout.argtypes = [P, P, P, P, P, I, I, I, I, F, I, P, F, U64, P]
+        L.fa_fwd_dropout.restype = I
+        L.fa_bwd_dropout.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, F, I, P, F, U64, P, Z, P]
+        L.fa_bwd_dropout.restype = I
         L.fa_fwd_f32.argtypes = L.fa_fwd.argtypes
         L.fa_fwd_f32.restype = I
         L.fa_bwd_f32.argtypes = L.fa_bwd.argtypes
@@ -93,6 +101,18 @@ def fa_bwd_dq(q, k, v, lse, dout, dq, B, H, N, d, scale, causal, blockmask, work
               workspace_bytes, stream) -> int:
     return lib().fa_bwd_dq(q, k, v, lse, dout, dq, B, H, N, d, scale, causal, blockmask,
                            workspace, workspace_bytes, stream)
+
+
+def fa_fwd_dropout(q, k, v, o, lse, B, H, N, d, scale, causal, blockmask, p_drop, seed,
+                   stream) -> int:
+    return lib().fa_fwd_dropout(q, k, v, o, lse, B, H, N, d, scale, causal, blockmask, p_drop,
+                                seed, stream)
+
+
+def fa_bwd_dropout(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, blockmask,
+                   p_drop, seed, workspace, workspace_bytes, stream) -> int:
+    return lib().fa_bwd_dropout(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal,
+                                blockmask, p_drop, seed, workspace, workspace_bytes, stream)
 
 
 def fa_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal, blockmask, stream) -> int:
@@ -195,6 +215,42 @@ def bwd_stages(q, k, v, o, lse, dout, scale, causal=False, blockmask=None, grads
     _check(fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dout), _ptr(dq), B, H, N, d,
                      float(scale), int(causal), _ptr(blockmask), _ptr(workspace), wn, s),
            "fa_bwd_dq")
+    return dq, dk, dv
+
+
+def fwd_dropout(q, k, v, scale, p_drop, seed, causal=False, blockmask=None, out=None, lse=None,
+                stream=None):
+    """bf16 forward with dropout on P: returns (O bf16, lse fp32)."""
+    import torch
+
+    B, H, N, d = _shape(q)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check(fa_fwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, float(scale),
+                          int(causal), _ptr(blockmask), float(p_drop), int(seed), _stream(stream)),
+           "fa_fwd_dropout")
+    return out, lse
+
+
+def bwd_dropout(q, k, v, o, lse, dout, scale, p_drop, seed, causal=False, blockmask=None,
+                grads=None, workspace=None, stream=None):
+    """bf16 backward of fwd_dropout (same p_drop and seed): returns (dQ, dK, dV), fp32."""
+    import torch
+
+    B, H, N, d = _shape(q)
+    if grads is None:
+        grads = tuple(torch.empty(q.shape, dtype=torch.float32, device=q.device) for _ in range(3))
+    dq, dk, dv = grads
+    wsb = fa_bwd_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=q.device)
+    _check(fa_bwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                          _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(causal),
+                          _ptr(blockmask), float(p_drop), int(seed), _ptr(workspace),
+                          workspace.numel() * workspace.element_size(), _stream(stream)),
+           "fa_bwd_dropout")
     return dq, dk, dv
 
 

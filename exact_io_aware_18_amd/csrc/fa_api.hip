@@ -69,65 +69,96 @@ int launched() {
 }
 
 // ---- bf16 forward -----------------------------------------------------------
-template <int D, bool CAUSAL, bool MASK>
+template <int D, bool CAUSAL, bool MASK, bool DROP>
 void launch_fwd_t(const fa::FwdArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((fa::fwd_bf16_kernel<D, CAUSAL, MASK>), dim3(grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((fa::fwd_bf16_kernel<D, CAUSAL, MASK, DROP>), dim3(grid), dim3(256), 0, s, a);
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP>
 void launch_fwd_pp(fa::FwdArgs a, int BH, hipStream_t s) {
   a.nqt = (a.N + fa::FwdPPTile<D>::BR - 1) / fa::FwdPPTile<D>::BR;
   a.total = BH * a.nqt;
-  hipLaunchKernelGGL((fa::fwd_pp_kernel<D, CAUSAL>), dim3(a.total), dim3(fa::FwdPPTile<D>::NT), 0, s, a);
+  hipLaunchKernelGGL((fa::fwd_pp_kernel<D, CAUSAL, DROP>), dim3(a.total), dim3(fa::FwdPPTile<D>::NT), 0, s, a);
 }
 
 // Dense and causal use the ping-pong kernel (256 query rows per workgroup);
 // a block mask needs 128-row workgroups (one mask row each).
-template <int D>
-void launch_fwd_d(const fa::FwdArgs& a, int BH, bool causal, bool mask, hipStream_t s) {
+template <int D, bool DROP>
+void launch_fwd_dd(const fa::FwdArgs& a, int BH, bool causal, bool mask, hipStream_t s) {
   if (mask) {
-    if (causal) launch_fwd_t<D, true, true>(a, a.total, s);
-    else launch_fwd_t<D, false, true>(a, a.total, s);
+    if (causal) launch_fwd_t<D, true, true, DROP>(a, a.total, s);
+    else launch_fwd_t<D, false, true, DROP>(a, a.total, s);
   } else {
-    if (causal) launch_fwd_pp<D, true>(a, BH, s);
-    else launch_fwd_pp<D, false>(a, BH, s);
+    if (causal) launch_fwd_pp<D, true, DROP>(a, BH, s);
+    else launch_fwd_pp<D, false, DROP>(a, BH, s);
   }
+}
+
+template <int D>
+void launch_fwd_d(const fa::FwdArgs& a, int BH, bool causal, bool mask, bool drop, hipStream_t s) {
+  if (drop) launch_fwd_dd<D, true>(a, BH, causal, mask, s);
+  else launch_fwd_dd<D, false>(a, BH, causal, mask, s);
 }
 
 // ---- bf16 backward ----------------------------------------------------------
 enum BwdStage { kPre = 1, kDkdv = 2, kDq = 4 };
 
-template <int D, bool CAUSAL, bool MASK>
+template <int D, bool CAUSAL, bool MASK, bool DROP>
 void launch_bwd_t(fa::BwdArgs a, int BH, int stages, hipStream_t s) {
   a.total = BH * a.ntile;
   if (stages & kDkdv)
-    hipLaunchKernelGGL((fa::bwd_dkdv_kernel<D, CAUSAL, MASK>), dim3(a.total), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((fa::bwd_dkdv_kernel<D, CAUSAL, MASK, DROP>), dim3(a.total), dim3(256), 0, s, a);
   if (stages & kDq)
-    hipLaunchKernelGGL((fa::bwd_dq_kernel<D, CAUSAL, MASK>), dim3(a.total), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((fa::bwd_dq_kernel<D, CAUSAL, MASK, DROP>), dim3(a.total), dim3(256), 0, s, a);
+}
+
+template <int D, bool DROP>
+void launch_bwd_dd(const fa::BwdArgs& a, int BH, bool causal, bool mask, int stages, hipStream_t s) {
+  if (causal) {
+    if (mask) launch_bwd_t<D, true, true, DROP>(a, BH, stages, s);
+    else launch_bwd_t<D, true, false, DROP>(a, BH, stages, s);
+  } else {
+    if (mask) launch_bwd_t<D, false, true, DROP>(a, BH, stages, s);
+    else launch_bwd_t<D, false, false, DROP>(a, BH, stages, s);
+  }
 }
 
 template <int D>
-void launch_bwd_d(const fa::BwdArgs& a, int BH, bool causal, bool mask, int stages, hipStream_t s) {
+void launch_bwd_d(const fa::BwdArgs& a, int BH, bool causal, bool mask, bool drop, int stages,
+                  hipStream_t s) {
   if (stages & kPre) {
     const long rows = (long)BH * a.N;
     const int pre_grid = (int)((rows * (D / 8) + 255) / 256);
     hipLaunchKernelGGL((fa::bwd_pre_kernel<D>), dim3(pre_grid), dim3(256), 0, s, a.o, a.dout, a.Dw, rows);
   }
-  if (causal) {
-    if (mask) launch_bwd_t<D, true, true>(a, BH, stages, s);
-    else launch_bwd_t<D, true, false>(a, BH, stages, s);
-  } else {
-    if (mask) launch_bwd_t<D, false, true>(a, BH, stages, s);
-    else launch_bwd_t<D, false, false>(a, BH, stages, s);
-  }
+  if (drop) launch_bwd_dd<D, true>(a, BH, causal, mask, stages, s);
+  else launch_bwd_dd<D, false>(a, BH, causal, mask, stages, s);
 }
 
-int run_bwd(const fa::BwdArgs& a, int BH, int d, int causal, bool mask, int stages, void* stream) {
+int run_bwd(const fa::BwdArgs& a, int BH, int d, int causal, bool mask, int stages, void* stream,
+            bool drop = false) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  if (d == 64) launch_bwd_d<64>(a, BH, causal, mask, stages, s);
-  else launch_bwd_d<128>(a, BH, causal, mask, stages, s);
+  if (d == 64) launch_bwd_d<64>(a, BH, causal, mask, drop, stages, s);
+  else launch_bwd_d<128>(a, BH, causal, mask, drop, stages, s);
   return launched();
+}
+
+// Dropout parameters: T = floor(p * 2^32) (the float p widened exactly to
+// double), keep scale 1 / (1 - p).
+int check_dropout(float p) {
+  if (!(p >= 0.f && p < 1.f)) return FA_ERR_DROPOUT;  // NaN fails both
+  return FA_OK;
+}
+
+fa::DropArgs drop_args(float p, unsigned long long seed) {
+  fa::DropArgs dp;
+  const double t = std::floor((double)p * 4294967296.0);
+  dp.thresh = t >= 4294967295.0 ? 0xFFFFFFFFu : (uint32_t)t;
+  dp.seed_lo = (uint32_t)(seed & 0xFFFFFFFFull);
+  dp.seed_hi = (uint32_t)(seed >> 32);
+  dp.keep_scale = (float)(1.0 / (1.0 - (double)p));
+  return dp;
 }
 
 // ---- fp32 -------------------------------------------------------------------
@@ -248,17 +279,13 @@ fa::BwdArgs bwd_args(const void* q, const void* k, const void* v, const void* o,
   a.total = 0;
   a.c = scale * fa::kLog2e;
   a.scale = scale;
+  a.drop = fa::DropArgs{0u, 0u, 0u, 1.f};
   return a;
 }
 
-}  // namespace
-
-extern "C" {
-
-int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
-           int d, float scale, int causal, const unsigned char* blockmask, void* stream) {
-  int st = check_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, blockmask, 2);
-  if (st) return st;
+int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+            int d, float scale, int causal, const unsigned char* blockmask, const fa::DropArgs* drop,
+            void* stream) {
   fa::FwdArgs a;
   a.q = static_cast<const __bf16*>(q);
   a.k = static_cast<const __bf16*>(k);
@@ -274,11 +301,35 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   // scaling; FLT_MIN times a finite score rounds 2^(score) to exactly 1.
   a.c = std::fmax(std::fabs(scale) * fa::kLog2e, FLT_MIN);
   a.negate_q = scale < 0.f;
+  a.drop = drop ? *drop : fa::DropArgs{0u, 0u, 0u, 1.f};
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  if (d == 64) launch_fwd_d<64>(a, B * H, causal, blockmask != nullptr, s);
-  else launch_fwd_d<128>(a, B * H, causal, blockmask != nullptr, s);
+  if (d == 64) launch_fwd_d<64>(a, B * H, causal, blockmask != nullptr, drop != nullptr, s);
+  else launch_fwd_d<128>(a, B * H, causal, blockmask != nullptr, drop != nullptr, s);
   return launched();
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+           int d, float scale, int causal, const unsigned char* blockmask, void* stream) {
+  int st = check_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, blockmask, 2);
+  if (st) return st;
+  return run_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, blockmask, nullptr, stream);
+}
+
+int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                   int N, int d, float scale, int causal, const unsigned char* blockmask,
+                   float p_drop, unsigned long long seed, void* stream) {
+  int st = check_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, blockmask, 2);
+  if (st) return st;
+  if ((st = check_dropout(p_drop))) return st;
+  if (p_drop == 0.f)  // every element kept: the plain kernels, bit for bit
+    return run_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, blockmask, nullptr, stream);
+  const fa::DropArgs dp = drop_args(p_drop, seed);
+  return run_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, blockmask, &dp, stream);
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -290,6 +341,20 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
   if (st) return st;
   const fa::BwdArgs a = bwd_args(q, k, v, o, lse, dout, dq, dk, dv, N, scale, blockmask, workspace);
   return run_bwd(a, B * H, d, causal, blockmask != nullptr, kPre | kDkdv | kDq, stream);
+}
+
+int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, float* dq, float* dk, float* dv, int B, int H, int N, int d,
+                   float scale, int causal, const unsigned char* blockmask, float p_drop,
+                   unsigned long long seed, void* workspace, size_t workspace_bytes_,
+                   void* stream) {
+  int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, blockmask,
+                     workspace, workspace_bytes_, 2);
+  if (st) return st;
+  if ((st = check_dropout(p_drop))) return st;
+  fa::BwdArgs a = bwd_args(q, k, v, o, lse, dout, dq, dk, dv, N, scale, blockmask, workspace);
+  a.drop = drop_args(p_drop, seed);
+  return run_bwd(a, B * H, d, causal, blockmask != nullptr, kPre | kDkdv | kDq, stream, p_drop != 0.f);
 }
 
 int fa_bwd_preprocess(const void* o, const void* dout, int B, int H, int N, int d,
@@ -413,6 +478,7 @@ const char* fa_strerror(int status) {
     case FA_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
     case FA_ERR_UNSUPPORTED: return "arguments are valid but not supported by this build";
     case FA_ERR_SCALE: return "scale must be finite";
+    case FA_ERR_DROPOUT: return "dropout probability must be in [0, 1)";
     default: return "unknown status";
   }
 }

@@ -45,7 +45,19 @@ struct BwdArgs {
   int total;            // workgroups in the grid
   float c;              // scale * log2(e) (signed)
   float scale;
+  DropArgs drop;        // used by the dropout instantiations only
 };
+
+// Keep bits, for the lane's key kj, of the four queries i0 .. i0+3 held by
+// accumulator rows of the S = Q K^T layout (lane = key): the four lanes of a
+// quad share the queries and hold four consecutive keys, so each computes
+// one generator call (query i0 + t, keys kj & ~3 ..) and the quad exchanges
+// the bits.
+__device__ __forceinline__ uint32_t keep4_keylane(const DropArgs& dp, int bh, int i0, int kj,
+                                                  int lane) {
+  const int t = lane & 3;
+  return quad_transpose4(keep4(dp, bh, i0 + t, kj & ~3), t);
+}
 
 // ---- D_i = sum_c dO_ic * O_ic ------------------------------------------------
 template <int D>
@@ -91,7 +103,7 @@ struct DkdvTile {
   static constexpr int MIN_WG = PIPE ? 1 : 2;
 };
 
-template <int D, bool CAUSAL, bool MASK>
+template <int D, bool CAUSAL, bool MASK, bool DROP>
 __global__ __launch_bounds__(256, DkdvTile<D>::MIN_WG) void bwd_dkdv_kernel(BwdArgs a) {
   using T = DkdvTile<D>;
   constexpr int NT = T::NT, BQ = T::BQ, BK = T::BK, PITCH = T::PITCH;
@@ -187,6 +199,11 @@ __global__ __launch_bounds__(256, DkdvTile<D>::MIN_WG) void bwd_dkdv_kernel(BwdA
       const f32x4 l1 = *reinterpret_cast<const f32x4*>(lt + 32 * sb + 16 * hf + 8 * h + 4);
       const f32x4 e0 = *reinterpret_cast<const f32x4*>(et + 32 * sb + 16 * hf + 8 * h);
       const f32x4 e1 = *reinterpret_cast<const f32x4*>(et + 32 * sb + 16 * hf + 8 * h + 4);
+      uint32_t kbits = 0xFFu;  // keep bits of rows 8hf .. 8hf+7
+      if constexpr (DROP) {
+        const int i0 = qs0 + 16 * hf + 8 * h;
+        kbits = keep4_keylane(a.drop, bh, i0, kj, lane) | (keep4_keylane(a.drop, bh, i0 + 4, kj, lane) << 4);
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int r = 8 * hf + e;
@@ -197,8 +214,14 @@ __global__ __launch_bounds__(256, DkdvTile<D>::MIN_WG) void bwd_dkdv_kernel(BwdA
           const int qq = qs0 + acc_row(r, h);
           if ((CAUSAL && kj > qq) || qq >= N) pv = 0.f;
         }
-        p[r] = pv;
-        dsv[r] = pv * (dP[r] - dvv);
+        if constexpr (DROP) {
+          const bool kept = (kbits >> e) & 1u;
+          p[r] = kept ? pv : 0.f;
+          dsv[r] = pv * ((kept ? dP[r] * a.drop.keep_scale : 0.f) - dvv);
+        } else {
+          p[r] = pv;
+          dsv[r] = pv * (dP[r] - dvv);
+        }
       }
     }
     pb[0] = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
@@ -304,6 +327,11 @@ __global__ __launch_bounds__(256, DkdvTile<D>::MIN_WG) void bwd_dkdv_kernel(BwdA
         const f32x4 l1 = *reinterpret_cast<const f32x4*>(lt + 32 * sb + 16 * hf + 8 * h + 4);
         const f32x4 e0 = *reinterpret_cast<const f32x4*>(et + 32 * sb + 16 * hf + 8 * h);
         const f32x4 e1 = *reinterpret_cast<const f32x4*>(et + 32 * sb + 16 * hf + 8 * h + 4);
+        uint32_t kbits = 0xFFu;
+        if constexpr (DROP) {
+          const int i0 = qs0 + 16 * hf + 8 * h;
+          kbits = keep4_keylane(a.drop, bh, i0, kj, lane) | (keep4_keylane(a.drop, bh, i0 + 4, kj, lane) << 4);
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int r = 8 * hf + e;
@@ -314,8 +342,14 @@ __global__ __launch_bounds__(256, DkdvTile<D>::MIN_WG) void bwd_dkdv_kernel(BwdA
             const int qq = qs0 + acc_row(r, h);
             if ((CAUSAL && kj > qq) || qq >= N) pv = 0.f;
           }
-          p[r] = pv;
-          dsv[r] = pv * (dP[r] - dvv);
+          if constexpr (DROP) {
+            const bool kept = (kbits >> e) & 1u;
+            p[r] = kept ? pv : 0.f;
+            dsv[r] = pv * ((kept ? dP[r] * a.drop.keep_scale : 0.f) - dvv);
+          } else {
+            p[r] = pv;
+            dsv[r] = pv * (dP[r] - dvv);
+          }
         }
       }
       const bf16x8 pb0 = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
@@ -410,8 +444,9 @@ __global__ __launch_bounds__(256, DkdvTile<D>::MIN_WG) void bwd_dkdv_kernel(BwdA
         f32x4* pv = reinterpret_cast<f32x4*>(dVrow + col);
         pk[0] = f32x4{dk[ct][r0] * sc, dk[ct][r0 + 1] * sc, dk[ct][r0 + 2] * sc, dk[ct][r0 + 3] * sc};
         pk[1] = f32x4{dk[ct][r0 + 4] * sc, dk[ct][r0 + 5] * sc, dk[ct][r0 + 6] * sc, dk[ct][r0 + 7] * sc};
-        pv[0] = f32x4{dv[ct][r0], dv[ct][r0 + 1], dv[ct][r0 + 2], dv[ct][r0 + 3]};
-        pv[1] = f32x4{dv[ct][r0 + 4], dv[ct][r0 + 5], dv[ct][r0 + 6], dv[ct][r0 + 7]};
+        const float vs = DROP ? a.drop.keep_scale : 1.f;  // dV = (P o Z)^T dO / (1 - p)
+        pv[0] = f32x4{dv[ct][r0] * vs, dv[ct][r0 + 1] * vs, dv[ct][r0 + 2] * vs, dv[ct][r0 + 3] * vs};
+        pv[1] = f32x4{dv[ct][r0 + 4] * vs, dv[ct][r0 + 5] * vs, dv[ct][r0 + 6] * vs, dv[ct][r0 + 7] * vs};
       }
   }
 }
@@ -433,7 +468,7 @@ struct DqTile {
   static constexpr int MIN_WG = 2;
 };
 
-template <int D, bool CAUSAL, bool MASK>
+template <int D, bool CAUSAL, bool MASK, bool DROP>
 __global__ __launch_bounds__(256, DqTile<D>::MIN_WG) void bwd_dq_kernel(BwdArgs a) {
   using T = DqTile<D>;
   constexpr int NT = T::NT, BR = T::BR, BC = T::BC, PITCH = T::PITCH;
@@ -508,6 +543,12 @@ __global__ __launch_bounds__(256, DqTile<D>::MIN_WG) void bwd_dq_kernel(BwdArgs 
         if (kc + 3 < NKC) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 5);
       }
       float dsv[16];
+      uint32_t kbits = 0xFFFFu;  // keep bits of rows 0..15 (keys k0 + 32 t2 + acc_row(r, h))
+      if constexpr (DROP) {
+        const int j0 = k0 + 32 * t2 + 8 * h;
+        kbits = keep4(a.drop, bh, qi, j0) | (keep4(a.drop, bh, qi, j0 + 4) << 4) |
+                (keep4(a.drop, bh, qi, j0 + 16) << 8) | (keep4(a.drop, bh, qi, j0 + 20) << 12);
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], c, -lse2));
@@ -515,7 +556,12 @@ __global__ __launch_bounds__(256, DqTile<D>::MIN_WG) void bwd_dq_kernel(BwdArgs 
           const int key = k0 + 32 * t2 + acc_row(r, h);
           if ((CAUSAL && key > qi) || key >= N) pv = 0.f;
         }
-        dsv[r] = pv * (dP[r] - Di);
+        if constexpr (DROP) {
+          const bool kept = (kbits >> r) & 1u;
+          dsv[r] = pv * ((kept ? dP[r] * a.drop.keep_scale : 0.f) - Di);
+        } else {
+          dsv[r] = pv * (dP[r] - Di);
+        }
       }
       dsb[2 * t2 + 0] = to_bf16x8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
       dsb[2 * t2 + 1] = to_bf16x8(dsv[8], dsv[9], dsv[10], dsv[11], dsv[12], dsv[13], dsv[14], dsv[15]);

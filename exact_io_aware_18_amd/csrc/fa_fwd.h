@@ -30,6 +30,7 @@
 #pragma once
 
 #include "fa_device.h"
+#include "fa_dropout.h"
 #include "fa_sched.h"
 
 namespace fa {
@@ -54,7 +55,19 @@ struct FwdArgs {
   int nb;               // mask blocks per side
   float c;              // max(|scale| * log2(e), FLT_MIN): masked scores stay -inf
   int negate_q;         // scale < 0: scores computed with -Q and |scale|
+  DropArgs drop;        // used by the dropout instantiations only
 };
+
+// Zero the dropped entries of the 8 probabilities p[0..7] that a lane holds
+// for query i and keys j0 .. j0+7 (j0 a multiple of 8).
+__device__ __forceinline__ void drop8(const DropArgs& dp, int bh, int i, int j0, float* p) {
+  const uint32_t lo = keep4(dp, bh, i, j0), hi = keep4(dp, bh, i, j0 + 4);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    p[e] = ((lo >> e) & 1u) ? p[e] : 0.f;
+    p[4 + e] = ((hi >> e) & 1u) ? p[4 + e] : 0.f;
+  }
+}
 
 template <int D>
 struct FwdTile {
@@ -74,7 +87,7 @@ struct FwdTile {
   static constexpr bool PIPE = (D == 64);
 };
 
-template <int D, bool CAUSAL, bool MASK>
+template <int D, bool CAUSAL, bool MASK, bool DROP>
 __global__ __launch_bounds__(256, FwdTile<D>::MIN_WG) void fwd_bf16_kernel(FwdArgs a) {
   using T = FwdTile<D>;
   constexpr int BC = T::BC, BR = T::BR, NT = T::NT, PITCH = T::PITCH;
@@ -223,10 +236,15 @@ __global__ __launch_bounds__(256, FwdTile<D>::MIN_WG) void fwd_bf16_kernel(FwdAr
         p0[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[8 * hh + e], c, -mb));
         p1[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[8 * hh + e], c, -mb));
       }
-      pb[hh] = to_bf16x8(p0[0], p0[1], p0[2], p0[3], p0[4], p0[5], p0[6], p0[7]);
-      pb[2 + hh] = to_bf16x8(p1[0], p1[1], p1[2], p1[3], p1[4], p1[5], p1[6], p1[7]);
+      // l sums the undropped probabilities; the product takes the kept ones
       lsum[hh] = ((p0[0] + p0[1]) + (p0[2] + p0[3])) + ((p0[4] + p0[5]) + (p0[6] + p0[7]));
       lsum[2 + hh] = ((p1[0] + p1[1]) + (p1[2] + p1[3])) + ((p1[4] + p1[5]) + (p1[6] + p1[7]));
+      if constexpr (DROP) {
+        drop8(a.drop, bh, qi, k0 + 16 * hh + 8 * h, p0);
+        drop8(a.drop, bh, qi, k0 + 32 + 16 * hh + 8 * h, p1);
+      }
+      pb[hh] = to_bf16x8(p0[0], p0[1], p0[2], p0[3], p0[4], p0[5], p0[6], p0[7]);
+      pb[2 + hh] = to_bf16x8(p1[0], p1[1], p1[2], p1[3], p1[4], p1[5], p1[6], p1[7]);
     }
     L += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
     if constexpr (T::PIPE) {
@@ -319,7 +337,7 @@ __global__ __launch_bounds__(256, FwdTile<D>::MIN_WG) void fwd_bf16_kernel(FwdAr
   const float Lt = xhalf_sum(L);
   if (qi < N) {
     const bool empty = !(Lt > 0.f);
-    const float inv = empty ? 0.f : 1.f / Lt;
+    const float inv = empty ? 0.f : (DROP ? a.drop.keep_scale : 1.f) / Lt;
     __bf16* Orow = a.o + head + (size_t)qi * D;
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
@@ -358,7 +376,7 @@ struct FwdPPTile {
   static constexpr int T_BYTES = BC * PITCH;
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   using T = FwdPPTile<D>;
   constexpr int BC = T::BC, BR = T::BR, NT = T::NT, PITCH = T::PITCH;
@@ -413,7 +431,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   bf16x8 pb[4];   // P of the previous tile (bf16)
 
   // matrix phase of round r: O^T += V^T P^T for tile r-1, then S^T of tile r
-  auto mphase = [&] __device__ (int r, const char* kt, const char* vprev) {
+  auto mphase = [&] __device__ (int r, const char* kt, const char* vprev) __attribute__((always_inline)) {
     if (r >= 1 && r - 1 < wtiles) {
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
@@ -452,7 +470,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   };
 
   // vector phase: softmax of the scores of tile r into pb
-  auto vphase = [&] __device__ (int r) {
+  auto vphase = [&] __device__ (int r) __attribute__((always_inline)) {
     if (r < 0 || r >= wtiles) return;
     const int k0 = r * BC;
     const bool edge = (CAUSAL && k0 + BC - 1 > qw0) || (k0 + BC > N);
@@ -491,10 +509,14 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
         p0[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[8 * hh + e], c, -mb));
         p1[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[8 * hh + e], c, -mb));
       }
-      pb[hh] = to_bf16x8(p0[0], p0[1], p0[2], p0[3], p0[4], p0[5], p0[6], p0[7]);
-      pb[2 + hh] = to_bf16x8(p1[0], p1[1], p1[2], p1[3], p1[4], p1[5], p1[6], p1[7]);
       lsum[hh] = ((p0[0] + p0[1]) + (p0[2] + p0[3])) + ((p0[4] + p0[5]) + (p0[6] + p0[7]));
       lsum[2 + hh] = ((p1[0] + p1[1]) + (p1[2] + p1[3])) + ((p1[4] + p1[5]) + (p1[6] + p1[7]));
+      if constexpr (DROP) {
+        drop8(a.drop, bh, qi, k0 + 16 * hh + 8 * h, p0);
+        drop8(a.drop, bh, qi, k0 + 32 + 16 * hh + 8 * h, p1);
+      }
+      pb[hh] = to_bf16x8(p0[0], p0[1], p0[2], p0[3], p0[4], p0[5], p0[6], p0[7]);
+      pb[2 + hh] = to_bf16x8(p1[0], p1[1], p1[2], p1[3], p1[4], p1[5], p1[6], p1[7]);
     }
     L += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
   };
@@ -507,12 +529,12 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   // round r (r = 0 .. ntiles): K(r) in kb[r&1], V(r-1) in vb[(r-1)&1].
   // Each group runs its own loop (the phase order differs); both execute the
   // same two barriers per round.
-  auto copies = [&] __device__ (int r, char* knext, char* vcur) {
+  auto copies = [&] __device__ (int r, char* knext, char* vcur) __attribute__((always_inline)) {
     if (r + 1 < ntiles) cp.issue(knext, Kh, (r + 1) * BC, N, w);
     if (r < ntiles) cp.issue(vcur, Vh, r * BC, N, w);
   };
   if (grpA) {
-    auto roundA = [&] __device__ (int r, const char* kcur, char* knext, const char* vprev, char* vcur) {
+    auto roundA = [&] __device__ (int r, const char* kcur, char* knext, const char* vprev, char* vcur) __attribute__((always_inline)) {
       copies(r, knext, vcur);
       mphase(r, kcur, vprev);
       __syncthreads();
@@ -525,7 +547,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
       if (r + 1 <= ntiles) roundA(r + 1, kb1, kb0, vb0, vb1);
     }
   } else {
-    auto roundB = [&] __device__ (int r, const char* kcur, char* knext, const char* vprev, char* vcur) {
+    auto roundB = [&] __device__ (int r, const char* kcur, char* knext, const char* vprev, char* vcur) __attribute__((always_inline)) {
       copies(r, knext, vcur);
       vphase(r - 1);
       __syncthreads();
@@ -542,7 +564,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   const float Lt = xhalf_sum(L);
   if (qi < N) {
     const bool empty = !(Lt > 0.f);
-    const float inv = empty ? 0.f : 1.f / Lt;
+    const float inv = empty ? 0.f : (DROP ? a.drop.keep_scale : 1.f) / Lt;
     __bf16* Orow = a.o + head + (size_t)qi * D;
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)

@@ -62,7 +62,8 @@ typedef enum {
     FA_ERR_FLAG = -7,        /* causal is not 0 or 1 */
     FA_ERR_LAUNCH = -8,      /* the HIP runtime rejected a kernel launch */
     FA_ERR_UNSUPPORTED = -9, /* valid arguments this build does not handle */
-    FA_ERR_SCALE = -10       /* scale is NaN or infinite */
+    FA_ERR_SCALE = -10,      /* scale is NaN or infinite */
+    FA_ERR_DROPOUT = -11     /* p_drop is NaN or outside [0, 1) */
 } fa_status;
 
 /*
@@ -108,6 +109,33 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
               const void* dout, float* dq, int B, int H, int N, int d, float scale,
               int causal, const unsigned char* blockmask, const void* workspace,
               size_t workspace_bytes, void* stream);
+
+/*
+ * Forward and backward with dropout on the attention probabilities, bf16
+ * (the dropout stage of the fused kernel in the figure of "Flashattention
+ * fast and memory efficient exact attention with io awareness"):
+ *   O = (P o Z) V / (1 - p_drop),  P = softmax(scale * Q K^T, masked),
+ * lse = the logsumexp of the undropped scores (as for fa_fwd).  Z_ij is 1
+ * (kept) when word (j mod 4) of Philox-4x32-10 (Salmon et al., "Parallel
+ * random numbers: as easy as 1, 2, 3", SC 2011) at counter
+ * (j / 4, i, b*H + h, 0) and key (seed mod 2^32, seed / 2^32) is at least
+ * floor(p_drop * 2^32); i is the query and j the key index within the head.
+ * The mask is regenerated, never stored: fa_bwd_dropout must get the same
+ * p_drop and seed as the forward that produced o and lse, and computes the
+ * exact gradient for that mask (dV = (P o Z)^T dO / (1 - p),
+ * dP = (dO V^T) o Z / (1 - p), dS = P o (dP - D)).  Other arguments,
+ * layouts, ownership and errors as for fa_fwd / fa_bwd; p_drop must lie in
+ * [0, 1) (else FA_ERR_DROPOUT).  p_drop = 0 gives exactly fa_fwd / fa_bwd.
+ */
+int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int N, int d, float scale, int causal,
+                   const unsigned char* blockmask, float p_drop,
+                   unsigned long long seed, void* stream);
+int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
+                   const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                   int B, int H, int N, int d, float scale, int causal,
+                   const unsigned char* blockmask, float p_drop, unsigned long long seed,
+                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of workspace fa_bwd and fa_bwd_f32 need (0 for invalid sizes). */
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);

@@ -193,3 +193,35 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(fa, "LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(ImportError):
         fa.lib()
+
+
+@pytest.mark.parametrize("p", [1.0, 1.5, -0.1, float("nan"), float("inf")])
+def test_dropout_calls_reject_probability(lib, p):
+    a = fwd_args()
+    assert fa.fa_fwd_dropout(a["q"], a["k"], a["v"], a["o"], a["lse"], 1, 2, 256, 64, 0.125, 0,
+                             None, p, 7, None) == -11
+    b = bwd_args()
+    assert fa.fa_bwd_dropout(b["q"], b["k"], b["v"], b["o"], b["lse"], b["dout"], b["dq"], b["dk"],
+                             b["dv"], 1, 2, 256, 64, 0.125, 1, None, p, 7, b["workspace"],
+                             b["workspace_bytes"], None) == -11
+
+
+def test_dropout_calls_check_the_common_arguments_first(lib):
+    a = fwd_args()
+    f = lambda **o: fa.fa_fwd_dropout(o.get("q", a["q"]), a["k"], a["v"], o.get("o", a["o"]),
+                                      a["lse"], 1, 2, 256, o.get("d", 64), 0.125, o.get("causal", 0),
+                                      None, o.get("p", 0.1), 7, None)
+    assert f(q=None) == -1
+    assert f(d=96) == -3
+    assert f(causal=2) == -7
+    assert f(o=a["q"]) == -5
+    assert f(d=96, p=2.0) == -3  # shape errors come before the probability check
+    b = bwd_args()
+    g = lambda **o: fa.fa_bwd_dropout(b["q"], b["k"], b["v"], b["o"], b["lse"], b["dout"],
+                                      o.get("dq", b["dq"]), b["dk"], b["dv"], 1, 2, 256, 64, 0.125,
+                                      1, None, 0.1, 2**64 - 1, o.get("ws", b["workspace"]),
+                                      o.get("wn", b["workspace_bytes"]), None)
+    assert g(dq=None) == -1
+    assert g(wn=8) == -6
+    assert g(dq=b["q"]) == -5
+    assert g(ws=None) == -6

@@ -1,0 +1,123 @@
+"""Dropout on the attention probabilities: the HIP path (fa_fwd_dropout /
+fa_bwd_dropout through the C ABI) against the fp64 dropout oracle.
+
+Besides tolerance parity, the keep mask itself is compared bit for bit: with
+V (or dO) set to identity rows, O[i, j] (or dV[j, i]) is P_ij Z_ij / (1 - p),
+so its zero pattern is the mask the kernel used.
+"""
+import numpy as np
+import pytest
+import torch
+
+from exact_io_aware_18_amd.inputs import default_scale, make_blockmask, make_qkvdo, workload_inputs
+from oracle.dropout import attention_bwd_dropout, attention_fwd_dropout, keep_mask
+from tests.gpu_helpers import check, device, to64
+
+pytestmark = pytest.mark.gpu
+
+SEED = (1 << 40) + 123
+
+
+def run_drop(q, k, v, do, scale, causal, mask, p, seed, dev, backward=True):
+    import exact_io_aware_18_amd as fa
+
+    qg, kg, vg, dog = (t.to(dev) for t in (q, k, v, do))
+    mg = None if mask is None else mask.to(dev)
+    o, lse = fa.fwd_dropout(qg, kg, vg, scale, p, seed, causal, mg)
+    out = {"o": o, "lse": lse}
+    if backward:
+        out["dq"], out["dk"], out["dv"] = fa.bwd_dropout(qg, kg, vg, o, lse, dog, scale, p, seed,
+                                                         causal, mg)
+    torch.cuda.synchronize()
+    return {k_: v_.cpu() for k_, v_ in out.items()}
+
+
+def parity(q, k, v, do, scale, causal, mask, p, seed):
+    dev = device()
+    print(f"\n[dropout] shape={tuple(q.shape)} causal={causal} mask={mask is not None} p={p}",
+          flush=True)
+    got = run_drop(q, k, v, do, scale, causal, mask, p, seed, dev)
+    q64, k64, v64, do64 = (to64(t) for t in (q, k, v, do))
+    m = None if mask is None else mask.numpy()
+    o_ref, lse_ref = attention_fwd_dropout(q64, k64, v64, scale, causal, m, p, seed)
+    dq, dk, dv = attention_bwd_dropout(q64, k64, v64, do64, scale, causal, m, p, seed)
+    rep = {}
+    check("o", to64(got["o"]), o_ref, "bf16", rep)
+    check("lse", to64(got["lse"]), lse_ref, "bf16", rep)
+    check("dq", to64(got["dq"]), dq, "bf16", rep)
+    check("dk", to64(got["dk"]), dk, "bf16", rep)
+    check("dv", to64(got["dv"]), dv, "bf16", rep)
+    print("[dropout] max-abs:", {k_: f"{v_:.2e}" for k_, v_ in rep.items()}, flush=True)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("p", [0.1, 0.5])
+def test_dropout_parity_ragged(d, causal, p):
+    q, k, v, do = make_qkvdo(2, 3, 300, d, "bf16", seed=11)
+    parity(q, k, v, do, default_scale(d), causal, None, p, SEED)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_dropout_parity_block_mask(d):
+    N = 1000
+    q, k, v, do = make_qkvdo(1, 2, N, d, "bf16", seed=12)
+    mask = make_blockmask(N, 0.25, seed=3)
+    parity(q, k, v, do, default_scale(d), False, mask, 0.2, 99)
+
+
+def test_dropout_parity_gpt2_shape():
+    q, k, v, do, scale, causal, mask = workload_inputs("gpt2_small")
+    parity(q, k, v, do, scale, causal, mask, 0.1, SEED)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_dropout_mask_bits_exact(d, causal):
+    """N = d keys with V = I and dO = I: the zero patterns of O and dV are the
+    keep masks of the forward and of the dK/dV kernel, compared exactly."""
+    dev = device()
+    N, H, p = d, 3, 0.5
+    q, k, _, _ = make_qkvdo(1, H, N, d, "bf16", seed=21)
+    q, k = 0.25 * q.float(), 0.25 * k.float()  # flat softmax: no probability underflows
+    q, k = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    eye = torch.eye(N, d).expand(1, H, N, d).contiguous().to(torch.bfloat16)
+    got = run_drop(q, k, eye, eye, default_scale(d), causal, None, p, SEED, dev)
+    rows = np.arange(N)
+    for h in range(H):
+        z = keep_mask(h, rows, rows, p, SEED)
+        if causal:
+            z = z & (rows[None, :] <= rows[:, None])
+        o_nz = to64(got["o"])[0, h, :, :N] != 0
+        dv_nz = to64(got["dv"])[0, h, :N, :N].T != 0
+        assert np.array_equal(o_nz, z), f"forward mask differs in head {h}: {np.argwhere(o_nz != z)[:5]}"
+        assert np.array_equal(dv_nz, z), f"dK/dV mask differs in head {h}: {np.argwhere(dv_nz != z)[:5]}"
+        assert 0.3 < z.mean() < 0.7 or causal
+
+
+def test_zero_probability_is_the_plain_path():
+    import exact_io_aware_18_amd as fa
+
+    dev = device()
+    q, k, v, do = (t.to(dev) for t in make_qkvdo(1, 2, 200, 64, "bf16", seed=5))
+    o0, l0 = fa.fwd(q, k, v, 0.125, True)
+    o1, l1 = fa.fwd_dropout(q, k, v, 0.125, 0.0, SEED, True)
+    g0 = fa.bwd(q, k, v, o0, l0, do, 0.125, True)
+    g1 = fa.bwd_dropout(q, k, v, o1, l1, do, 0.125, 0.0, SEED, True)
+    torch.cuda.synchronize()
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)
+    for a, b in zip(g0, g1):
+        assert torch.equal(a, b)
+
+
+def test_dropout_is_repeatable_and_seeded():
+    import exact_io_aware_18_amd as fa
+
+    dev = device()
+    q, k, v, do = (t.to(dev) for t in make_qkvdo(1, 2, 256, 64, "bf16", seed=6))
+    a = fa.fwd_dropout(q, k, v, 0.125, 0.3, 1234, False)[0].clone()
+    b = fa.fwd_dropout(q, k, v, 0.125, 0.3, 1234, False)[0].clone()
+    c = fa.fwd_dropout(q, k, v, 0.125, 0.3, 1235, False)[0].clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    assert not torch.equal(a, c)
