@@ -192,6 +192,86 @@ def cpu_baseline(sub_names):
     }
 
 
+SPARSITY_FRACS = [0.0, 1 / 64, 1 / 32, 1 / 16, 1 / 8, 1 / 4, 1 / 2, 1.0]
+IO_SEQS = [2048, 4096, 8192, 16384]
+
+
+def _time_calls(fn, reps):
+    """Mean ms of `reps` back-to-back calls of fn(), HIP events on the current stream."""
+    import torch
+
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def sweep(kind, reps):
+    """Block-sparsity and IO sweeps: one JSON line per point.
+
+    sparsity: B=1, H=16, N=16384, d=64, block masks keeping the diagonal plus a
+      fraction f of the off-diagonal 128x128 blocks; forward and backward time
+      against the number of unmasked pairs (runtime should follow density).
+    io: B=1, H=16, non-causal, d=64 and 128, N in IO_SEQS, forward only, with
+      two query-tile heights: Br=256 (the ping-pong kernel, no mask) and
+      Br=128 (the block-mask kernel with an all-ones mask, the same result).
+      Run under rocprofv3 --pmc to read the bytes each launch moves; the
+      launches come in the printed order, `reps` + 1 per point.
+    """
+    import torch
+
+    import exact_io_aware_18_amd as fa
+    from exact_io_aware_18_amd.inputs import default_scale, make_blockmask, make_qkvdo
+
+    fa.lib()
+    dev = torch.device("cuda:0")
+    if kind == "sparsity":
+        B, H, N, d = 1, 16, 16384, 64
+        q, k, v, do = (t.to(dev) for t in make_qkvdo(B, H, N, d, "bf16", seed=0))
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        grads = tuple(torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(3))
+        ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+        for f in SPARSITY_FRACS:
+            mcpu = make_blockmask(N, f, seed=1)
+            m = mcpu.to(dev)
+            pairs = B * H * pairs_per_head(N, False, mcpu)
+            tf = _time_calls(lambda: fa.fwd(q, k, v, default_scale(d), False, m, out=o, lse=lse), reps)
+            tb = _time_calls(lambda: fa.bwd(q, k, v, o, lse, do, default_scale(d), False, m,
+                                            grads=grads, workspace=ws), reps)
+            print(json.dumps({"sweep": "sparsity", "B": B, "H": H, "N": N, "d": d, "frac": f,
+                              "density": round(float(mcpu.float().mean()), 6), "pairs": pairs,
+                              "fwd_ms": round(tf, 4), "bwd_ms": round(tb, 4),
+                              "fwd_tflops": round(4.0 * d * pairs / tf / 1e9, 1),
+                              "bwd_tflops": round(10.0 * d * pairs / tb / 1e9, 1)}), flush=True)
+    elif kind == "io":
+        B, H = 1, 16
+        for d in (64, 128):
+            for N in IO_SEQS:
+                q, k, v, _ = (t.to(dev) for t in make_qkvdo(B, H, N, d, "bf16", seed=0))
+                o = torch.empty_like(q)
+                lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+                nb = (N + 127) // 128
+                ones = torch.ones((nb, nb), dtype=torch.uint8, device=dev)
+                for br, m in ((256, None), (128, ones)):
+                    t = _time_calls(lambda: fa.fwd(q, k, v, default_scale(d), False, m, out=o, lse=lse), reps)
+                    # bytes of the tiled algorithm without cache reuse: K and V
+                    # read once per query tile, Q read and O, lse written once
+                    model = B * H * ((N // br) * 2 * N * d * 2 + 2 * N * d * 2 + N * 4)
+                    print(json.dumps({"sweep": "io", "B": B, "H": H, "N": N, "d": d, "Br": br,
+                                      "fwd_ms": round(t, 4),
+                                      "tflops": round(4.0 * d * B * H * N * N / t / 1e9, 1),
+                                      "io_model_bytes": model,
+                                      "compulsory_bytes": B * H * (4 * N * d * 2 + N * 4)}), flush=True)
+    else:
+        raise SystemExit(f"unknown sweep {kind}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -199,6 +279,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long_causal_16k", choices=sorted(BENCH_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", choices=["sparsity", "io"],
+                    help="run a block-sparsity or IO sweep instead of the step (one JSON line per point)")
+    ap.add_argument("--sweep-reps", type=int, default=10)
+    ap.add_argument("--dropout", type=float, default=0.0,
+                    help="dropout probability on P: the step becomes fa_fwd_dropout + "
+                         "fa_bwd_dropout per sub-workload, each timed as one call")
     ap.add_argument("--cold-steps", type=int, default=5,
                     help="extra steps, each after writing %d MiB of scratch (outside the timed "
                          "region), so that no input is cache-resident; reported per kernel as "
@@ -214,6 +300,10 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.sweep:
+        sweep(args.sweep, args.sweep_reps)
+        return
 
     if args.copy_calibration:
         x = torch.empty(args.copy_calibration << 20, dtype=torch.uint8, device="cuda:0")
@@ -246,9 +336,26 @@ def main():
         subs.append(sub)
 
     stream = torch.cuda.current_stream()
-    nk = 4  # kernels per sub-workload per step
+    drop = args.dropout
+    nk = 2 if drop > 0 else 4  # timed calls per sub-workload per step
+    seed = 0x5EED0000DEADBEEF
+
+    def step_dropout(events=None):
+        for si, s in enumerate(subs):
+            if events is not None:
+                events[si * nk].record(stream)
+            fa.fwd_dropout(s["q"], s["k"], s["v"], s["scale"], drop, seed, s["causal"], s["mask"],
+                           out=s["o"], lse=s["lse"])
+            if events is not None:
+                events[si * nk + 1].record(stream)
+            fa.bwd_dropout(s["q"], s["k"], s["v"], s["o"], s["lse"], s["do"], s["scale"], drop, seed,
+                           s["causal"], s["mask"], grads=s["grads"], workspace=s["ws"])
+        if events is not None:
+            events[len(subs) * nk].record(stream)
 
     def step(events=None):
+        if drop > 0:
+            return step_dropout(events)
         for si, s in enumerate(subs):
             base = si * nk
             if events is not None:
@@ -304,7 +411,7 @@ def main():
         torch.cuda.synchronize()
         del flush
 
-    kinds = ["fwd", "bwd_pre", "bwd_dkdv", "bwd_dq"]
+    kinds = ["fwd_dropout", "bwd_dropout"] if drop > 0 else ["fwd", "bwd_pre", "bwd_dkdv", "bwd_dq"]
     kernels = {}
     for si, s in enumerate(subs):
         for j, kind in enumerate(kinds):
@@ -317,8 +424,10 @@ def main():
             if cold:
                 kernels[key]["cold_ms"] = sorted(ev[a].elapsed_time(ev[a + 1]) for ev in cold)[len(cold) // 2]
             d, p, rows = s["d"], s["pairs"], s["B"] * s["H"] * s["N"]
-            if kind == "fwd":
+            if kind in ("fwd", "fwd_dropout"):
                 kernels[key]["flops"] = 4.0 * d * p
+            elif kind == "bwd_dropout":  # one call: preprocess, dK/dV and dQ kernels
+                kernels[key]["flops"] = 10.0 * d * p
             elif kind == "bwd_dkdv":
                 kernels[key]["flops"] = 8.0 * d * p
             elif kind == "bwd_dq":
@@ -332,7 +441,7 @@ def main():
 
     fwd_flops = sum(4.0 * s["d"] * s["pairs"] for s in subs)
     bwd_flops = sum(10.0 * s["d"] * s["pairs"] for s in subs)
-    fwd_ms = sum(kernels[f"fwd_d{s['d']}"]["ms"] for s in subs)
+    fwd_ms = sum(kernels[f"{kinds[0]}_d{s['d']}"]["ms"] for s in subs)
     value = (fwd_flops + bwd_flops) / (ms_per_step * 1e-3) / 1e12
 
     dom = max(kernels, key=lambda k_: kernels[k_]["ms"])
@@ -363,6 +472,7 @@ def main():
             "subs": [f"{s['name']}: B={s['B']} H={s['H']} N={s['N']} d={s['d']} "
                      f"causal={int(s['causal'])} mask={int(s['mask'] is not None)}" for s in subs],
             "parallelism": "single GPU",
+            "dropout": drop,
         },
         "fwd_tflops": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 2),
         "fwd_frac_peak": round(fwd_flops / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
