@@ -5,10 +5,11 @@ bench.py's CPU-baseline leg.  The library never imports it, and it imports
 nothing from the library.
 
 Functions and the passages they follow are documented in oracle/attention.py
-(attention) and oracle/dropout.py (dropout on the attention probabilities,
-with its counter-based generator).
-Every function here is pinned by tests/test_oracle_pins.py and
-tests/test_oracle_dropout_pins.py against closed
+(attention), oracle/dropout.py (dropout on the attention probabilities, with
+its counter-based generator) and oracle/decode.py (few queries against a long
+key/value cache).
+Every function here is pinned by tests/test_oracle_pins.py,
+tests/test_oracle_dropout_pins.py and tests/test_oracle_decode_pins.py against closed
 forms, brute force, finite differences and an independent library
 implementation; none is "parity unpinned".
 """
@@ -28,3 +29,4 @@ from .dropout import (  # noqa: F401
     keep_mask,
     philox4x32_10,
 )
+from .decode import attention_fwd_decode  # noqa: F401
