@@ -42,7 +42,7 @@ BENCH_WORKLOADS = {
     "blocksparse_64k": ["blocksparse_64k"],
 }
 
-KERNEL_SOURCES = ["fa_device.h", "fa_sched.h", "fa_dropout.h", "fa_fwd.h", "fa_bwd.h", "fa_api.hip"]
+KERNEL_SOURCES = ["fa_device.h", "fa_sched.h", "fa_dropout.h", "fa_fwd.h", "fa_bwd.h", "fa_decode.h", "fa_api.hip"]
 
 
 def kernel_source_hash() -> str:

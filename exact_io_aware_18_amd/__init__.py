@@ -6,10 +6,11 @@ memory and the current stream.  If the shared library is missing, every call
 raises; there is no fallback implementation.
 
 Low level: one function per exported symbol (fa_fwd, fa_bwd, the three
-backward stages, fa_fwd_dropout, fa_bwd_dropout, fa_fwd_f32, fa_bwd_f32,
-fa_bwd_workspace_bytes, fa_strerror, fa_version) takes the C arguments as they
-are (pointers as integers).  High level: fwd, bwd, bwd_stages, fwd_dropout,
-bwd_dropout, fwd_f32 and bwd_f32 take torch tensors, allocate the outputs and
+backward stages, fa_fwd_dropout, fa_bwd_dropout, fa_fwd_decode,
+fa_decode_workspace_bytes, fa_fwd_f32, fa_bwd_f32, fa_bwd_workspace_bytes,
+fa_strerror, fa_version) takes the C arguments as they are (pointers as
+integers).  High level: fwd, bwd, bwd_stages, fwd_dropout, bwd_dropout,
+decode, fwd_f32 and bwd_f32 take torch tensors, allocate the outputs and
 raise FAError on a nonzero status.
 """
 from __future__ import annotations
@@ -27,7 +28,8 @@ STATUS_NAMES = {
     -8: "FA_ERR_LAUNCH", -9: "FA_ERR_UNSUPPORTED", -10: "FA_ERR_SCALE", -11: "FA_ERR_DROPOUT",
 }
 EXPORTED = ("fa_fwd", "fa_bwd", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq",
-            "fa_fwd_dropout", "fa_bwd_dropout", "fa_bwd_workspace_bytes", "fa_fwd_f32",
+            "fa_fwd_dropout", "fa_bwd_dropout", "fa_fwd_decode", "fa_decode_workspace_bytes",
+            "fa_bwd_workspace_bytes", "fa_fwd_f32",
             "fa_bwd_f32", "fa_strerror", "fa_version")
 
 _lib = None
@@ -62,6 +64,10 @@ def lib() -> ctypes.CDLL:
         L.fa_fwd_dropout.restype = I
         L.fa_bwd_dropout.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, F, I, P, F, U64, P, Z, P]
         L.fa_bwd_dropout.restype = I
+        L.fa_fwd_decode.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P, Z, P]
+        L.fa_fwd_decode.restype = I
+        L.fa_decode_workspace_bytes.argtypes = [I, I, I, I, I]
+        L.fa_decode_workspace_bytes.restype = Z
         L.fa_fwd_f32.argtypes = L.fa_fwd.argtypes
         L.fa_fwd_f32.restype = I
         L.fa_bwd_f32.argtypes = L.fa_bwd.argtypes
@@ -113,6 +119,16 @@ def fa_bwd_dropout(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal,
                    p_drop, seed, workspace, workspace_bytes, stream) -> int:
     return lib().fa_bwd_dropout(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal,
                                 blockmask, p_drop, seed, workspace, workspace_bytes, stream)
+
+
+def fa_fwd_decode(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, workspace, workspace_bytes,
+                  stream) -> int:
+    return lib().fa_fwd_decode(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, workspace,
+                               workspace_bytes, stream)
+
+
+def fa_decode_workspace_bytes(B, H, Nq, Nk, d) -> int:
+    return lib().fa_decode_workspace_bytes(B, H, Nq, Nk, d)
 
 
 def fa_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal, blockmask, stream) -> int:
@@ -252,6 +268,26 @@ def bwd_dropout(q, k, v, o, lse, dout, scale, p_drop, seed, causal=False, blockm
                           workspace.numel() * workspace.element_size(), _stream(stream)),
            "fa_bwd_dropout")
     return dq, dk, dv
+
+
+def decode(q, k, v, scale, causal=False, out=None, lse=None, workspace=None, stream=None):
+    """bf16 decode: q [B,H,Nq,d] against k, v [B,H,Nk,d]; returns (O bf16, lse fp32)."""
+    import torch
+
+    B, H, Nq, d = _shape(q)
+    Nk = int(k.shape[2])
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(max(fa_decode_workspace_bytes(B, H, Nq, Nk, d), 1), dtype=torch.uint8,
+                                device=q.device)
+    _check(fa_fwd_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, d,
+                         float(scale), int(causal), _ptr(workspace),
+                         workspace.numel() * workspace.element_size(), _stream(stream)),
+           "fa_fwd_decode")
+    return out, lse
 
 
 def fwd_f32(q, k, v, scale, causal=False, blockmask=None, out=None, lse=None, stream=None):

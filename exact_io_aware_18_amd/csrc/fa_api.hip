@@ -9,6 +9,7 @@
 
 #include "fa.h"
 #include "fa_bwd.h"
+#include "fa_decode.h"
 #include "fa_f32.h"
 #include "fa_fwd.h"
 
@@ -258,6 +259,35 @@ int check_bwd(const void* q, const void* k, const void* v, const void* o, const 
   return check_bufs(ins, 7, outs, 4);
 }
 
+// ---- decode ------------------------------------------------------------------
+int check_decode_shape(int B, int H, int Nq, int Nk, int d) {
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if ((long long)Nk * d >= (1LL << 31) || (long long)Nq * d >= (1LL << 31)) return FA_ERR_SHAPE;
+  const long long bh = (long long)B * H;
+  if (bh * ((Nq + 31) / 32) * ((Nk + 255) / 256) >= (1LL << 31)) return FA_ERR_SHAPE;
+  if (bh * Nk * d >= (1LL << 46)) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+size_t decode_ws_bytes(int B, int H, int Nq, int Nk, int d) {
+  int nsplit, chunk;
+  fa::decode_split(B * H, Nq, Nk, d, &nsplit, &chunk);
+  const size_t rows = (size_t)B * H * Nq * nsplit;
+  const size_t lse_bytes = (rows * sizeof(float) + 255) & ~(size_t)255;
+  return lse_bytes + rows * d * sizeof(float);
+}
+
+template <int D>
+void launch_decode_d(const fa::DecArgs& a, int BH, bool causal, hipStream_t s) {
+  const unsigned grid = (unsigned)((long)BH * a.nqg * a.nsplit);
+  if (causal) hipLaunchKernelGGL((fa::decode_split_kernel<D, true>), dim3(grid), dim3(64), 0, s, a);
+  else hipLaunchKernelGGL((fa::decode_split_kernel<D, false>), dim3(grid), dim3(64), 0, s, a);
+  const long rows = (long)BH * a.Nq;
+  const unsigned mgrid = (unsigned)((rows * (D / 4) + 255) / 256);
+  hipLaunchKernelGGL((fa::decode_merge_kernel<D>), dim3(mgrid), dim3(256), 0, s, a, rows);
+}
+
 fa::BwdArgs bwd_args(const void* q, const void* k, const void* v, const void* o,
                      const float* lse, const void* dout, float* dq, float* dk, float* dv,
                      int N, float scale, const unsigned char* mask, void* ws) {
@@ -406,6 +436,48 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const float* lse, con
   const fa::BwdArgs a = bwd_args(q, k, v, nullptr, lse, dout, dq, nullptr, nullptr, N, scale,
                                  blockmask, const_cast<void*>(workspace));
   return run_bwd(a, B * H, d, causal, blockmask != nullptr, kDq, stream);
+}
+
+int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                  int Nq, int Nk, int d, float scale, int causal, void* workspace,
+                  size_t workspace_bytes_, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  int st = check_decode_shape(B, H, Nq, Nk, d);
+  if (st) return st;
+  if ((st = check_flags(scale, causal))) return st;
+  const size_t need = decode_ws_bytes(B, H, Nq, Nk, d);
+  if (!workspace || workspace_bytes_ < need) return FA_ERR_WORKSPACE;
+  const size_t tq = (size_t)B * H * Nq * d * 2, tk = (size_t)B * H * Nk * d * 2;
+  const Buf ins[3] = {{q, tq, 16}, {k, tk, 16}, {v, tk, 16}};
+  const Buf outs[3] = {{o, tq, 16}, {lse, (size_t)B * H * Nq * 4, 4}, {workspace, need, 16}};
+  if ((st = check_bufs(ins, 3, outs, 3))) return st;
+  fa::DecArgs a;
+  a.q = static_cast<const __bf16*>(q);
+  a.k = static_cast<const __bf16*>(k);
+  a.v = static_cast<const __bf16*>(v);
+  a.o = static_cast<__bf16*>(o);
+  a.lse = lse;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.nqg = (Nq + 31) / 32;
+  fa::decode_split(B * H, Nq, Nk, d, &a.nsplit, &a.chunk);
+  const size_t rows = (size_t)B * H * Nq * a.nsplit;
+  a.part_lse = static_cast<float*>(workspace);
+  a.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                      ((rows * sizeof(float) + 255) & ~(size_t)255));
+  a.off = Nk - Nq;
+  a.c = std::fmax(std::fabs(scale) * fa::kLog2e, FLT_MIN);
+  a.negate_q = scale < 0.f;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (d == 64) launch_decode_d<64>(a, B * H, causal != 0, s);
+  else launch_decode_d<128>(a, B * H, causal != 0, s);
+  return launched();
+}
+
+size_t fa_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d) {
+  if (check_decode_shape(B, H, Nq, Nk, d) != FA_OK) return 0;
+  return decode_ws_bytes(B, H, Nq, Nk, d);
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {

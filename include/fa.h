@@ -137,6 +137,27 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
                    const unsigned char* blockmask, float p_drop, unsigned long long seed,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Decode: Nq new queries per (batch, head) against a cache of Nk keys and
+ * values (Flash-Decoding, named on the aggregator page "Flashattention fast
+ * and memory efficient exact attention with io awareness").  q: bf16
+ * [B,H,Nq,d]; k, v: bf16 [B,H,Nk,d]; o: bf16 [B,H,Nq,d]; lse: fp32 [B,H,Nq].
+ * Computes O = softmax(scale * Q K^T) V.  With causal = 1, query i is
+ * sequence position i + Nk - Nq and sees keys j <= i + Nk - Nq (a query
+ * with no visible key gets O = 0, lse = -inf).  The keys are split into
+ * chunks processed in parallel and the partial results merged exactly
+ * (lse = log sum exp of the parts).  workspace: device memory of at least
+ * fa_decode_workspace_bytes(B,H,Nq,Nk,d) bytes, 16-byte aligned, holding
+ * the fp32 partials; contents on entry ignored, on exit unspecified.  No
+ * block mask.  Any Nq, Nk >= 1; errors as for fa_fwd, plus FA_ERR_WORKSPACE.
+ */
+int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace fa_fwd_decode needs (0 for invalid sizes). */
+size_t fa_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d);
+
 /* Bytes of workspace fa_bwd and fa_bwd_f32 need (0 for invalid sizes). */
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
 

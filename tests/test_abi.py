@@ -225,3 +225,37 @@ def test_dropout_calls_check_the_common_arguments_first(lib):
     assert g(wn=8) == -6
     assert g(dq=b["q"]) == -5
     assert g(ws=None) == -6
+
+
+def test_decode_workspace_bytes(lib):
+    assert fa.fa_decode_workspace_bytes(1, 1, 1, 1, 64) >= 4 * 65
+    assert fa.fa_decode_workspace_bytes(2, 8, 4, 100000, 128) >= 2 * 8 * 4 * 129 * 4
+    assert fa.fa_decode_workspace_bytes(1, 1, 0, 10, 64) == 0
+    assert fa.fa_decode_workspace_bytes(1, 1, 1, 0, 64) == 0
+    assert fa.fa_decode_workspace_bytes(1, 1, 1, 10, 80) == 0
+
+
+def test_decode_rejects(lib):
+    B, H, Nq, Nk, d = 2, 4, 3, 5000, 64
+    tq, tk = B * H * Nq * d * 2, B * H * Nk * d * 2
+    ws = fa.fa_decode_workspace_bytes(B, H, Nq, Nk, d)
+    a = dict(q=BASE, k=BASE + tq + MB, v=BASE + tq + tk + 2 * MB, o=BASE + tq + 2 * tk + 3 * MB,
+             lse=BASE + 2 * tq + 2 * tk + 4 * MB, ws=BASE + 2 * tq + 2 * tk + 5 * MB)
+
+    def call(**o):
+        x = dict(a, **o)
+        return fa.fa_fwd_decode(x["q"], x["k"], x["v"], x["o"], x["lse"], B, H, o.get("Nq", Nq),
+                                o.get("Nk", Nk), o.get("d", d), o.get("scale", 0.1),
+                                o.get("causal", 1), x["ws"], o.get("wn", ws), None)
+    assert call(q=None) == -1
+    assert call(o=None) == -1
+    assert call(Nq=0) == -2
+    assert call(Nk=-1) == -2
+    assert call(d=96) == -3
+    assert call(causal=4) == -7
+    assert call(scale=float("nan")) == -10
+    assert call(ws=None) == -6
+    assert call(wn=ws - 1) == -6
+    assert call(q=BASE + 4) == -4
+    assert call(o=a["k"] + 64) == -5
+    assert call(ws=a["o"]) == -5
