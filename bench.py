@@ -194,6 +194,9 @@ def cpu_baseline(sub_names):
 
 SPARSITY_FRACS = [0.0, 1 / 64, 1 / 32, 1 / 16, 1 / 8, 1 / 4, 1 / 2, 1.0]
 IO_SEQS = [2048, 4096, 8192, 16384]
+DECODE_POINTS = [(8, 32, 1, 4096, 128), (8, 32, 1, 16384, 128), (8, 32, 1, 65536, 128),
+                 (1, 32, 1, 1 << 20, 128), (8, 32, 8, 16384, 128), (8, 32, 1, 16384, 64),
+                 (64, 8, 1, 8192, 128)]
 
 
 def _time_calls(fn, reps):
@@ -268,6 +271,25 @@ def sweep(kind, reps):
                                       "tflops": round(4.0 * d * B * H * N * N / t / 1e9, 1),
                                       "io_model_bytes": model,
                                       "compulsory_bytes": B * H * (4 * N * d * 2 + N * 4)}), flush=True)
+    elif kind == "decode":
+        # few queries against a long cache: K and V are streamed once, so the
+        # bound is HBM bandwidth (bytes = K + V + Q + O + lse per call)
+        for (B, H, nq, nk, d) in DECODE_POINTS:
+            g = torch.Generator().manual_seed(0)
+            q = torch.randn((B, H, nq, d), generator=g).to(torch.bfloat16).to(dev)
+            k = torch.randn((B, H, nk, d), generator=g).to(torch.bfloat16).to(dev)
+            v = torch.randn((B, H, nk, d), generator=g).to(torch.bfloat16).to(dev)
+            o = torch.empty_like(q)
+            lse = torch.empty((B, H, nq), dtype=torch.float32, device=dev)
+            ws = torch.empty(fa.fa_decode_workspace_bytes(B, H, nq, nk, d), dtype=torch.uint8, device=dev)
+            t = _time_calls(lambda: fa.decode(q, k, v, default_scale(d), True, out=o, lse=lse,
+                                              workspace=ws), reps)
+            nbytes = B * H * (2 * nk * d * 2 + 2 * nq * d * 2 + nq * 4)
+            print(json.dumps({"sweep": "decode", "B": B, "H": H, "Nq": nq, "Nk": nk, "d": d,
+                              "causal": True, "ms": round(t, 4), "bytes": nbytes,
+                              "gbs": round(nbytes / t / 1e6, 1),
+                              "frac_hbm_peak": round(nbytes / t / 1e6 / PEAK_HBM_GBS, 4)}), flush=True)
+            del q, k, v, o, lse, ws
     else:
         raise SystemExit(f"unknown sweep {kind}")
 
@@ -351,7 +373,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long_causal_16k", choices=sorted(BENCH_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--sweep", choices=["sparsity", "io"],
+    ap.add_argument("--sweep", choices=["sparsity", "io", "decode"],
                     help="run a block-sparsity or IO sweep instead of the step (one JSON line per point)")
     ap.add_argument("--sweep-reps", type=int, default=10)
     ap.add_argument("--baseline", choices=["standard"],
