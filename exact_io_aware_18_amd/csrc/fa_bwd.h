@@ -274,21 +274,21 @@ __global__ __launch_bounds__(256, DkdvTile<D>::MIN_WG) void bwd_dkdv_kernel(BwdA
     // phase C: accumulate(0) on the matrix pipe, grads(1) on the VALU
     accumulate(qt, dt, pb0, sv0);
     grads(edge_c, S1, dP1, lt, et, 1, q0, pb1, sv1);
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 5);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 12, 5);
 #pragma unroll
     for (int m = 0; m < 4 * NCT; ++m) {
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 5);
       __builtin_amdgcn_sched_group_barrier(kSchedValu, 80 / (4 * NCT), 5);
-      if (m + 2 < 4 * NCT) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 5);
+      if (m + 6 < 4 * NCT) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 5);
     }
     __builtin_amdgcn_sched_barrier(0);
     // phase D: accumulate(1)
     accumulate(qs1, ds1, pb1, sv1);
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 6);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 12, 6);
 #pragma unroll
     for (int m = 0; m < 4 * NCT; ++m) {
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 6);
-      if (m + 2 < 4 * NCT) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 6);
+      if (m + 6 < 4 * NCT) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 6);
     }
   };
 
