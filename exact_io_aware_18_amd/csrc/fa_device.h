@@ -1,6 +1,7 @@
 // Device-side building blocks for the gfx950 attention kernels: MFMA
 // wrappers, the lane/row permutation that keeps softmax rows in registers,
-// LDS swizzles, tile staging and wave-level reductions.
+// the LDS tile swizzle, direct-to-LDS tile copies, operand reads and
+// wave-level reductions.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -12,7 +13,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -39,15 +39,6 @@ __device__ __forceinline__ int perm32(int x) {
 // Source row held in register r by half-wave h after perm32-loaded rows.
 __device__ __forceinline__ int acc_row(int r, int h) {
   return ((r >> 3) << 4) | (h << 3) | (r & 7);
-}
-
-// XOR swizzle of 16-byte chunks inside an LDS row.  Rows read together by
-// eight (or sixteen) consecutive lanes through perm32 map to distinct
-// chunks, so a ds_read_b128 wave touches distinct banks.
-__device__ __forceinline__ int swz(int row, int chunk, int nchunk) {
-  const int b3 = (row >> 3) & 1;
-  const int f = ((row & 7) ^ (b3 << 2)) | (b3 << 3);
-  return chunk ^ (f & (nchunk - 1));
 }
 
 // XOR swizzle of the 16-byte chunks of a natural [rows][D] bf16 LDS tile.
@@ -91,36 +82,12 @@ __device__ __forceinline__ float xhalf_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// Sum of the eight bf16 values of v (as fp32) added to acc: four v_dot2 ops.
-__device__ __forceinline__ float sum8(bf16x8 v, float acc) {
-  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-  float a0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one, acc, false);
-  float a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one, 0.f, false);
-  a0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one, a0, false);
-  a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one, a1, false);
-  return a0 + a1;
-}
-
 __device__ __forceinline__ bf16x8 lds_read16(const char* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
 
-__device__ __forceinline__ void lds_write16(char* p, u32x4 v) {
-  *reinterpret_cast<u32x4*>(p) = v;
-}
-
-__device__ __forceinline__ void lds_write8(char* p, u32x2 v) {
-  *reinterpret_cast<u32x2*>(p) = v;
-}
-
 __device__ __forceinline__ u32x4 gload16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
-}
-
-__device__ __forceinline__ u32x2 gload8(const void* p) {
-  return *reinterpret_cast<const u32x2*>(p);
 }
 
 // Eight fp32 values -> eight bf16, round to nearest even (v_cvt_pk_bf16_f32).
@@ -131,15 +98,6 @@ __device__ __forceinline__ bf16x8 to_bf16x8(float a0, float a1, float a2, float 
   r[4] = (__bf16)a4; r[5] = (__bf16)a5; r[6] = (__bf16)a6; r[7] = (__bf16)a7;
   return r;
 }
-
-// Registers r0 .. r0+7 of an accumulator as bf16x8.
-__device__ __forceinline__ bf16x8 acc_to_bf16(const f32x16& c, int r0) {
-  return to_bf16x8(c[r0 + 0], c[r0 + 1], c[r0 + 2], c[r0 + 3],
-                   c[r0 + 4], c[r0 + 5], c[r0 + 6], c[r0 + 7]);
-}
-
-// Value held by lane l ^ 32.
-__device__ __forceinline__ float xhalf(float x) { return __shfl_xor(x, 32); }
 
 __device__ __forceinline__ bool wave_any(bool p) {
   return __builtin_amdgcn_ballot_w64(p) != 0;
@@ -152,115 +110,6 @@ __device__ __forceinline__ int xcd_remap(int g, int total) {
   const int x = g & 7, s = g >> 3;
   const int q = total >> 3, r = total & 7;
   return (x < r) ? x * (q + 1) + s : r * (q + 1) + (x - r) * q + s;
-}
-
-// ---- 4x4 bf16 block transpose ----------------------------------------------
-// rows[e] holds elements (row e, cols 0..3) of a 4x4 block; returns in
-// out[t] the elements (rows 0..3, col t).
-__device__ __forceinline__ void transpose4x4(const u32x2 rows[4], u32x2 out[4]) {
-  out[0] = u32x2{(rows[0].x & 0xffffu) | (rows[1].x << 16), (rows[2].x & 0xffffu) | (rows[3].x << 16)};
-  out[1] = u32x2{(rows[0].x >> 16) | (rows[1].x & 0xffff0000u), (rows[2].x >> 16) | (rows[3].x & 0xffff0000u)};
-  out[2] = u32x2{(rows[0].y & 0xffffu) | (rows[1].y << 16), (rows[2].y & 0xffffu) | (rows[3].y << 16)};
-  out[3] = u32x2{(rows[0].y >> 16) | (rows[1].y & 0xffff0000u), (rows[2].y >> 16) | (rows[3].y & 0xffff0000u)};
-}
-
-// ---- tile staging -----------------------------------------------------------
-// A tile of ROWS consecutive sequence rows x D columns (bf16) is staged by
-// NT threads.  Natural layout in LDS: [ROWS][D], pitch 2*D bytes, 16-byte
-// chunks swizzled by swz(row, .).  Transposed layout: [D][ROWS], pitch
-// 2*ROWS bytes, chunks swizzled by swz(col, .).  Rows at or beyond `nvalid`
-// are staged as zeros.
-
-// Natural layout only, 16-byte pieces.
-template <int ROWS, int D, int NT>
-struct StageRows16 {
-  static constexpr int CH = D / 8;                 // 16-byte chunks per row
-  static constexpr int NCHUNK = ROWS * CH;
-  static constexpr int PER = (NCHUNK + NT - 1) / NT;   // chunks per thread
-  static_assert(NCHUNK % NT == 0 || NCHUNK < NT, "tile must divide evenly");
-  u32x4 r[PER];
-
-  __device__ __forceinline__ void load(const __bf16* src, int row0, int nvalid, int tid) {
-#pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      const int u = tid + NT * e;
-      const int row = u / CH, ch = u % CH;
-      if (u < NCHUNK && row0 + row < nvalid)
-        r[e] = gload16(src + (size_t)(row0 + row) * D + ch * 8);
-      else
-        r[e] = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-  __device__ __forceinline__ void store(char* lds, int tid) const {
-#pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      const int u = tid + NT * e;
-      const int row = u / CH, ch = u % CH;
-      if (u < NCHUNK) lds_write16(lds + row * (2 * D) + swz(row, ch, CH) * 16, r[e]);
-    }
-  }
-};
-
-// 4x4 blocks, written in natural and/or transposed layout.
-template <int ROWS, int D, int NT>
-struct StageBlocks4 {
-  static constexpr int CG = D / 4;                 // 4-column groups per row
-  static constexpr int NBLK = (ROWS / 4) * CG;
-  static constexpr int PER = (NBLK + NT - 1) / NT;
-  static_assert(NBLK % NT == 0 || NBLK < NT, "tile must divide evenly");
-  u32x2 r[PER][4];
-
-  __device__ __forceinline__ void load(const __bf16* src, int row0, int nvalid, int tid) {
-#pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      const int blk = tid + NT * e;
-      const int c0 = 4 * (blk % CG), j0 = 4 * (blk / CG);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        if (blk < NBLK && row0 + j0 + t < nvalid)
-          r[e][t] = gload8(src + (size_t)(row0 + j0 + t) * D + c0);
-        else
-          r[e][t] = u32x2{0u, 0u};
-      }
-    }
-  }
-  __device__ __forceinline__ void store_nat(char* lds, int tid) const {
-    constexpr int CH = D / 8;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      const int blk = tid + NT * e;
-      if (blk >= NBLK) continue;
-      const int c0 = 4 * (blk % CG), j0 = 4 * (blk / CG);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int row = j0 + t;
-        lds_write8(lds + row * (2 * D) + swz(row, c0 >> 3, CH) * 16 + ((c0 >> 2) & 1) * 8, r[e][t]);
-      }
-    }
-  }
-  __device__ __forceinline__ void store_tr(char* lds, int tid) const {
-    constexpr int CH = ROWS / 8;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      const int blk = tid + NT * e;
-      if (blk >= NBLK) continue;
-      const int c0 = 4 * (blk % CG), j0 = 4 * (blk / CG);
-      u32x2 t4[4];
-      transpose4x4(r[e], t4);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int row = c0 + t;
-        lds_write8(lds + row * (2 * ROWS) + swz(row, j0 >> 3, CH) * 16 + ((j0 >> 2) & 1) * 8, t4[t]);
-      }
-    }
-  }
-};
-
-// Read the 16-byte MFMA operand slice (row, logical chunk) of a swizzled tile.
-template <int PITCH_BYTES>
-__device__ __forceinline__ bf16x8 tile_read(const char* lds, int row, int chunk) {
-  constexpr int CH = PITCH_BYTES / 16;
-  return lds_read16(lds + row * PITCH_BYTES + swz(row, chunk, CH) * 16);
 }
 
 // 16-byte direct-to-LDS copy (global_load_lds_dwordx4): lane l of the wave

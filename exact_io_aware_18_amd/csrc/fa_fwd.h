@@ -1,6 +1,9 @@
-// Forward attention kernel for gfx950, bf16 inputs, fp32 accumulation.
+// Forward attention kernels for gfx950, bf16 inputs, fp32 accumulation.
 //
-// One workgroup owns 128 query rows of one (batch, head); each of its four
+// fwd_pp_kernel (dense and causal): 256 query rows per workgroup, eight
+// waves in two groups that alternate matrix and vector phases (described at
+// the kernel).  fwd_bf16_kernel (block mask): one workgroup owns 128 query
+// rows of one (batch, head), one mask row; each of its four
 // waves owns 32 of them and keeps its Q fragment in registers for the whole
 // kernel.  K/V tiles of 64 keys are copied HBM -> LDS by direct-to-LDS loads
 // (global_load_lds_dwordx4) into two buffers, so the copy of tile t+1 runs
