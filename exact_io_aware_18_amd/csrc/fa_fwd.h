@@ -39,6 +39,9 @@
 namespace fa {
 
 constexpr float kLazyTau = 8.0f;  // log2 units: P values stay below 2^8
+// A tile whose probabilities against the current reference sum (per lane,
+// 32 keys) to at most this needs no row max (P then stays below 2^14).
+constexpr float kSkipSum = 16384.0f;
 
 // instruction classes for __builtin_amdgcn_sched_group_barrier
 constexpr int kSchedValu = 0x002;
@@ -485,43 +488,66 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
         if ((CAUSAL && key1 > qi) || key1 >= N) s1[e] = -INFINITY;
       }
     }
-    float m0 = fmaxf(s0[0], s0[1]), m1 = fmaxf(s1[0], s1[1]);
+    // P = 2^(S*c - Mref) against the current reference.  The row max is
+    // needed only when a row has no reference yet or some P of this tile
+    // would exceed 2^kSkipLog2: then the reference moves (lazily, as in the
+    // other kernel) and P is recomputed.  Either way O / l and lse use the
+    // same reference, so the result does not depend on which path ran.
+    float p0[16], p1[16];
+    auto exps = [&] __device__ (float mb) __attribute__((always_inline)) -> float {
+      float ls[4];
 #pragma unroll
-    for (int e = 2; e < 16; e += 2) {
-      m0 = fmaxf(fmaxf(m0, s0[e]), s0[e + 1]);
-      m1 = fmaxf(fmaxf(m1, s1[e]), s1[e + 1]);
-    }
-    const float mx = xhalf_max(fmaxf(m0, m1));
-    const float mt = (mx == -INFINITY) ? -INFINITY : mx * c;
-    const bool need = mt > Mref + kLazyTau;
-    if (wave_any(need)) {
-      const float Mn = need ? mt : Mref;
-      const float alpha = need ? __builtin_amdgcn_exp2f(Mref - Mn) : 1.f;
-      L *= alpha;
+      for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) o[ct] *= alpha;
-      Mref = Mn;
+        for (int e = 0; e < 8; ++e) {
+          p0[8 * hh + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[8 * hh + e], c, -mb));
+          p1[8 * hh + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[8 * hh + e], c, -mb));
+        }
+        const float* a0 = p0 + 8 * hh;
+        const float* a1 = p1 + 8 * hh;
+        ls[hh] = ((a0[0] + a0[1]) + (a0[2] + a0[3])) + ((a0[4] + a0[5]) + (a0[6] + a0[7]));
+        ls[2 + hh] = ((a1[0] + a1[1]) + (a1[2] + a1[3])) + ((a1[4] + a1[5]) + (a1[6] + a1[7]));
+      }
+      return (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    };
+    bool slow = wave_any(Mref == -INFINITY);
+    float lt = 0.f;
+    if (!slow) {
+      lt = exps(Mref);
+      slow = wave_any(!(lt <= kSkipSum));  // also catches inf / NaN
     }
-    const float mb = (Mref == -INFINITY) ? 0.f : Mref;
-    float lsum[4];
+    if (slow) {
+      float m0 = fmaxf(s0[0], s0[1]), m1 = fmaxf(s1[0], s1[1]);
+#pragma unroll
+      for (int e = 2; e < 16; e += 2) {
+        m0 = fmaxf(fmaxf(m0, s0[e]), s0[e + 1]);
+        m1 = fmaxf(fmaxf(m1, s1[e]), s1[e + 1]);
+      }
+      const float mx = xhalf_max(fmaxf(m0, m1));
+      const float mt = (mx == -INFINITY) ? -INFINITY : mx * c;
+      const bool need = mt > Mref + kLazyTau;
+      if (wave_any(need)) {
+        const float Mn = need ? mt : Mref;
+        const float alpha = need ? __builtin_amdgcn_exp2f(Mref - Mn) : 1.f;
+        L *= alpha;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) o[ct] *= alpha;
+        Mref = Mn;
+      }
+      lt = exps((Mref == -INFINITY) ? 0.f : Mref);
+    }
+    L += lt;
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      float p0[8], p1[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        p0[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[8 * hh + e], c, -mb));
-        p1[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[8 * hh + e], c, -mb));
-      }
-      lsum[hh] = ((p0[0] + p0[1]) + (p0[2] + p0[3])) + ((p0[4] + p0[5]) + (p0[6] + p0[7]));
-      lsum[2 + hh] = ((p1[0] + p1[1]) + (p1[2] + p1[3])) + ((p1[4] + p1[5]) + (p1[6] + p1[7]));
       if constexpr (DROP) {
-        drop8(a.drop, bh, qi, k0 + 16 * hh + 8 * h, p0);
-        drop8(a.drop, bh, qi, k0 + 32 + 16 * hh + 8 * h, p1);
+        drop8(a.drop, bh, qi, k0 + 16 * hh + 8 * h, p0 + 8 * hh);
+        drop8(a.drop, bh, qi, k0 + 32 + 16 * hh + 8 * h, p1 + 8 * hh);
       }
-      pb[hh] = to_bf16x8(p0[0], p0[1], p0[2], p0[3], p0[4], p0[5], p0[6], p0[7]);
-      pb[2 + hh] = to_bf16x8(p1[0], p1[1], p1[2], p1[3], p1[4], p1[5], p1[6], p1[7]);
+      const float* a0 = p0 + 8 * hh;
+      const float* a1 = p1 + 8 * hh;
+      pb[hh] = to_bf16x8(a0[0], a0[1], a0[2], a0[3], a0[4], a0[5], a0[6], a0[7]);
+      pb[2 + hh] = to_bf16x8(a1[0], a1[1], a1[2], a1[3], a1[4], a1[5], a1[6], a1[7]);
     }
-    L += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
   };
 
   // prologue: K(0) into kb0

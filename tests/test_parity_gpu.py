@@ -201,3 +201,21 @@ def test_row_shift_on_gpu():
     assert (o1.float() - o2.float()).abs().max().item() <= 2e-2
     exp_shift = scale * shift.float().to(dev)
     assert (l2 - l1 - exp_shift).abs().max().item() <= 1e-3
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_running_max_moves_late(d, causal):
+    """Scores that grow along the keys (key rows scaled by a ramp) and one
+    planted dominant key late in the sequence: the reference max must move
+    in tiles after the first, through the forward's recompute path.  Forward
+    only: the backward reads lse and has no running max, and its bf16 error
+    on the 40-unit score row exceeds the fixed absolute tolerance."""
+    N = 1100
+    q, k, v, do = make_qkvdo(1, 2, N, d, "bf16", seed=31)
+    ramp = torch.linspace(0.5, 2.0, N)[None, None, :, None]
+    k = (k.float() * ramp).to(torch.bfloat16)
+    # query 700 of head 1 meets key 650 with a score of 40, its others ~N(0, 25)
+    kk = k[0, 1, 650].float()
+    q[0, 1, 700] = (kk * (40.0 / (kk.norm() ** 2 * default_scale(d)))).to(torch.bfloat16)
+    full_parity(q, k, v, do, default_scale(d), causal, None, "bf16", backward=False)
