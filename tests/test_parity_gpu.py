@@ -219,3 +219,13 @@ def test_running_max_moves_late(d, causal):
     kk = k[0, 1, 650].float()
     q[0, 1, 700] = (kk * (40.0 / (kk.norm() ** 2 * default_scale(d)))).to(torch.bfloat16)
     full_parity(q, k, v, do, default_scale(d), causal, None, "bf16", backward=False)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_pingpong_grid_sizes(d, causal):
+    """A grid of exactly 512 ping-pong workgroups (B*H = 128, N = 1000), the
+    smallest that takes the 256-row kernel; smaller grids (the other
+    full-parity tests) take the 128-row kernel."""
+    q, k, v, do = make_qkvdo(2, 64, 1000, d, "bf16", seed=41)
+    full_parity(q, k, v, do, default_scale(d), causal, None, "bf16")
