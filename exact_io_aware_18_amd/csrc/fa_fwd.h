@@ -195,25 +195,34 @@ __global__ __launch_bounds__(256, FwdTile<D>::MIN_WG) void fwd_bf16_kernel(FwdAr
         if ((CAUSAL && key1 > qi) || key1 >= N) s1[r] = -INFINITY;
       }
     }
-    // ---- row max over the tile (v_max3 chains), shared by both halves
-    float m0 = fmaxf(s0[0], s0[1]), m1 = fmaxf(s1[0], s1[1]);
+    // ---- P = 2^(S*c - Mref) against the current reference, its fp32 row
+    // sum and its bf16 copy for the product.  The row max is taken only when
+    // a row has no reference yet or a P of this tile would exceed 2^14 (the
+    // tile is then recomputed after the max, below).
+    bf16x8 pb[4];
+    auto make_p = [&] __device__ (float mb) __attribute__((always_inline)) -> float {
+      float lsum[4];
 #pragma unroll
-    for (int r = 2; r < 16; r += 2) {
-      m0 = fmaxf(fmaxf(m0, s0[r]), s0[r + 1]);
-      m1 = fmaxf(fmaxf(m1, s1[r]), s1[r + 1]);
-    }
-    const float mx = xhalf_max(fmaxf(m0, m1));
-    const float mt = (mx == -INFINITY) ? -INFINITY : mx * c;
-    const bool need = mt > Mref + kLazyTau;
-    if (wave_any(need)) {
-      const float Mn = need ? mt : Mref;
-      const float alpha = need ? __builtin_amdgcn_exp2f(Mref - Mn) : 1.f;
-      L *= alpha;
+      for (int hh = 0; hh < 2; ++hh) {
+        float p0[8], p1[8];
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) o[ct] *= alpha;
-      Mref = Mn;
-    }
-    const float mb = (Mref == -INFINITY) ? 0.f : Mref;
+        for (int e = 0; e < 8; ++e) {
+          p0[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[8 * hh + e], c, -mb));
+          p1[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[8 * hh + e], c, -mb));
+        }
+        // l sums the undropped probabilities; the product takes the kept ones
+        lsum[hh] = ((p0[0] + p0[1]) + (p0[2] + p0[3])) + ((p0[4] + p0[5]) + (p0[6] + p0[7]));
+        lsum[2 + hh] = ((p1[0] + p1[1]) + (p1[2] + p1[3])) + ((p1[4] + p1[5]) + (p1[6] + p1[7]));
+        if constexpr (DROP) {
+          drop8(a.drop, bh, qi, k0 + 16 * hh + 8 * h, p0);
+          drop8(a.drop, bh, qi, k0 + 32 + 16 * hh + 8 * h, p1);
+        }
+        pb[hh] = to_bf16x8(p0[0], p0[1], p0[2], p0[3], p0[4], p0[5], p0[6], p0[7]);
+        pb[2 + hh] = to_bf16x8(p1[0], p1[1], p1[2], p1[3], p1[4], p1[5], p1[6], p1[7]);
+      }
+      return (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+    };
+    const bool noref = wave_any(Mref == -INFINITY);
     // ---- S(next) on the matrix pipe ...
     if constexpr (T::PIPE) {
       bf16x8 ka0[NKC], ka1[NKC];
@@ -230,29 +239,8 @@ __global__ __launch_bounds__(256, FwdTile<D>::MIN_WG) void fwd_bf16_kernel(FwdAr
         n1 = mfma32(ka1[kc], qf[kc], n1);
       }
     }
-    // ---- ... while P = 2^(S*c - Mref) and l (fp32 tree) run on the VALU;
-    // the products take P rounded to bf16
-    bf16x8 pb[4];
-    float lsum[4];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      float p0[8], p1[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        p0[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[8 * hh + e], c, -mb));
-        p1[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[8 * hh + e], c, -mb));
-      }
-      // l sums the undropped probabilities; the product takes the kept ones
-      lsum[hh] = ((p0[0] + p0[1]) + (p0[2] + p0[3])) + ((p0[4] + p0[5]) + (p0[6] + p0[7]));
-      lsum[2 + hh] = ((p1[0] + p1[1]) + (p1[2] + p1[3])) + ((p1[4] + p1[5]) + (p1[6] + p1[7]));
-      if constexpr (DROP) {
-        drop8(a.drop, bh, qi, k0 + 16 * hh + 8 * h, p0);
-        drop8(a.drop, bh, qi, k0 + 32 + 16 * hh + 8 * h, p1);
-      }
-      pb[hh] = to_bf16x8(p0[0], p0[1], p0[2], p0[3], p0[4], p0[5], p0[6], p0[7]);
-      pb[2 + hh] = to_bf16x8(p1[0], p1[1], p1[2], p1[3], p1[4], p1[5], p1[6], p1[7]);
-    }
-    L += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+    // ---- ... while P runs on the VALU (discarded below when noref)
+    float lt = make_p(noref ? 0.f : Mref);
     if constexpr (T::PIPE) {
       // interleave: K reads three k-steps ahead, one MFMA per ~7 VALU ops
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 1);
@@ -266,6 +254,29 @@ __global__ __launch_bounds__(256, FwdTile<D>::MIN_WG) void fwd_bf16_kernel(FwdAr
       }
     }
     __builtin_amdgcn_sched_barrier(0);
+    // ---- rare: row max over the tile (v_max3 chains, both halves), lazy
+    // move of the reference with the rescale of O and l, P again
+    if (noref || wave_any(!(lt <= kSkipSum))) {
+      float m0 = fmaxf(s0[0], s0[1]), m1 = fmaxf(s1[0], s1[1]);
+#pragma unroll
+      for (int r = 2; r < 16; r += 2) {
+        m0 = fmaxf(fmaxf(m0, s0[r]), s0[r + 1]);
+        m1 = fmaxf(fmaxf(m1, s1[r]), s1[r + 1]);
+      }
+      const float mx = xhalf_max(fmaxf(m0, m1));
+      const float mt = (mx == -INFINITY) ? -INFINITY : mx * c;
+      const bool need = mt > Mref + kLazyTau;
+      if (wave_any(need)) {
+        const float Mn = need ? mt : Mref;
+        const float alpha = need ? __builtin_amdgcn_exp2f(Mref - Mn) : 1.f;
+        L *= alpha;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) o[ct] *= alpha;
+        Mref = Mn;
+      }
+      lt = make_p((Mref == -INFINITY) ? 0.f : Mref);
+    }
+    L += lt;
     // ---- O^T += V^T P^T, V reads two products ahead
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
