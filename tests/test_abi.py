@@ -259,3 +259,22 @@ def test_decode_rejects(lib):
     assert call(q=BASE + 4) == -4
     assert call(o=a["k"] + 64) == -5
     assert call(ws=a["o"]) == -5
+
+
+@pytest.mark.parametrize("compiler,lang,std", [("gcc", "c", "c99"), ("g++", "c++", "c++11")])
+def test_header_is_plain_c(compiler, lang, std, tmp_path):
+    """include/fa.h compiles as strict C99 and as C++ (no torch or HIP types
+    in the signatures), and a C translation unit can take every entry point's
+    address."""
+    import shutil
+
+    if shutil.which(compiler) is None:
+        pytest.skip(f"{compiler} not available")
+    src = tmp_path / ("use.c" if lang == "c" else "use.cpp")
+    names = declared_functions()
+    body = "\n".join(f"  (void)&{n};" for n in names)
+    src.write_text(f'#include "fa.h"\nint main(void) {{\n{body}\n  return 0;\n}}\n')
+    out = subprocess.run([compiler, f"-std={std}", "-Wall", "-Wextra", "-Werror", "-pedantic"
+                          if lang == "c" else "-Wall", "-fsyntax-only", "-I",
+                          os.path.join(ROOT, "include"), str(src)], capture_output=True, text=True)
+    assert out.returncode == 0, out.stderr
