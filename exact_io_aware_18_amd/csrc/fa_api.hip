@@ -117,8 +117,13 @@ enum BwdStage { kPre = 1, kDkdv = 2, kDq = 4 };
 template <int D, bool CAUSAL, bool MASK, bool DROP>
 void launch_bwd_t(fa::BwdArgs a, int BH, int stages, hipStream_t s) {
   a.total = BH * a.ntile;
-  if (stages & kDkdv)
-    hipLaunchKernelGGL((fa::bwd_dkdv_kernel<D, CAUSAL, MASK, DROP>), dim3(a.total), dim3(256), 0, s, a);
+  if (stages & kDkdv) {
+    if constexpr (D == 128)
+      hipLaunchKernelGGL((fa::bwd_dkdv_pair_kernel<D, CAUSAL, MASK, DROP>), dim3(a.total),
+                         dim3(fa::DkdvPairTile<D>::NT), 0, s, a);
+    else
+      hipLaunchKernelGGL((fa::bwd_dkdv_kernel<D, CAUSAL, MASK, DROP>), dim3(a.total), dim3(256), 0, s, a);
+  }
   if (stages & kDq)
     hipLaunchKernelGGL((fa::bwd_dq_kernel<D, CAUSAL, MASK, DROP>), dim3(a.total), dim3(256), 0, s, a);
 }

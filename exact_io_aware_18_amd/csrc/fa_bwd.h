@@ -13,7 +13,9 @@
 //   bwd_dkdv  one workgroup per 128 keys, loop over query tiles, dK and dV
 //             accumulated in registers (keys outer, queries inner, the loop
 //             order of the Figure 1 caption of "No More Quadratic Complexity
-//             for Transformers: Discover the Power of Flash Attention!")
+//             for Transformers: Discover the Power of Flash Attention!");
+//             one wave per 32 keys at d = 64, a wave pair per 32 keys at
+//             d = 128 (bwd_dkdv_pair_kernel)
 //   bwd_dq    one workgroup per 128 queries, loop over key tiles, dQ
 //             accumulated in registers (recomputes S and dP a second time
 //             instead of accumulating dQ with atomics)
@@ -80,7 +82,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__
   if (part == 0 && row < rows) Dw[row] = acc;
 }
 
-// ---- dK, dV: keys outer ----------------------------------------------------
+// ---- dK, dV: keys outer (d = 64) -------------------------------------------
 // One workgroup owns 128 keys (one mask block); each wave keeps the K and V
 // rows of its 32 keys in registers and accumulates dK^T and dV^T in
 // registers.  Query tiles of 64 rows (Q, dO, and per query lse*log2(e) and
@@ -96,11 +98,7 @@ struct DkdvTile {
   static constexpr int PITCH = 2 * D;
   static constexpr int T_BYTES = BQ * PITCH;
   static constexpr int LIST_CAP = 1024;
-  // d=128 pipelines the two 32-query sub-blocks of a tile, which needs the
-  // registers of one wave per SIMD; d=64 runs them one after the other with
-  // two waves per SIMD (measured faster at that size).
-  static constexpr bool PIPE = (D == 128);
-  static constexpr int MIN_WG = PIPE ? 1 : 2;
+  static constexpr int MIN_WG = 2;  // two waves per SIMD
 };
 
 template <int D, bool CAUSAL, bool MASK, bool DROP>
@@ -170,129 +168,7 @@ __global__ __launch_bounds__(256, DkdvTile<D>::MIN_WG) void bwd_dkdv_kernel(BwdA
     else if (w == 1) eb[lane] = x;
   };
 
-  // S = Q K^T and dP = dO V^T for the 32-query sub-block at `qs`/`ds`.
-  auto products = [&] __device__ (const char* qs, const char* ds, f32x16& S, f32x16& dP) {
-    bf16x8 aq[NKC], ad[NKC];
-#pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) {
-      aq[kc] = lds_read16(qs + toff.rows[kc]);
-      ad[kc] = lds_read16(ds + toff.rows[kc]);
-    }
-    S = f32x16{};
-    dP = f32x16{};
-#pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) {
-      S = mfma32(aq[kc], kf[kc], S);
-      dP = mfma32(ad[kc], vf[kc], dP);
-    }
-  };
-  // P = 2^(S*c - lse*log2 e) and dS = P o (dP - D) of sub-block sb, as bf16
-  // B operands (queries of the lane: 32sb + 16*hf + 8h + e).
-  auto grads = [&] __device__ (auto edge_c, const f32x16& S, const f32x16& dP, const float* lt,
-                               const float* et, int sb, int q0, bf16x8* pb, bf16x8* sbv) {
-    constexpr bool EDGE = decltype(edge_c)::value;
-    const int qs0 = q0 + 32 * sb;
-    float p[16], dsv[16];
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const f32x4 l0 = *reinterpret_cast<const f32x4*>(lt + 32 * sb + 16 * hf + 8 * h);
-      const f32x4 l1 = *reinterpret_cast<const f32x4*>(lt + 32 * sb + 16 * hf + 8 * h + 4);
-      const f32x4 e0 = *reinterpret_cast<const f32x4*>(et + 32 * sb + 16 * hf + 8 * h);
-      const f32x4 e1 = *reinterpret_cast<const f32x4*>(et + 32 * sb + 16 * hf + 8 * h + 4);
-      uint32_t kbits = 0xFFu;  // keep bits of rows 8hf .. 8hf+7
-      if constexpr (DROP) {
-        const int i0 = qs0 + 16 * hf + 8 * h;
-        kbits = keep4_keylane(a.drop, bh, i0, kj, lane) | (keep4_keylane(a.drop, bh, i0 + 4, kj, lane) << 4);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int r = 8 * hf + e;
-        const float lv = e < 4 ? l0[e] : l1[e - 4];
-        const float dvv = e < 4 ? e0[e] : e1[e - 4];
-        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], c, -lv));
-        if (EDGE) {
-          const int qq = qs0 + acc_row(r, h);
-          if ((CAUSAL && kj > qq) || qq >= N) pv = 0.f;
-        }
-        if constexpr (DROP) {
-          const bool kept = (kbits >> e) & 1u;
-          p[r] = kept ? pv : 0.f;
-          dsv[r] = pv * ((kept ? dP[r] * a.drop.keep_scale : 0.f) - dvv);
-        } else {
-          p[r] = pv;
-          dsv[r] = pv * (dP[r] - dvv);
-        }
-      }
-    }
-    pb[0] = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-    pb[1] = to_bf16x8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
-    sbv[0] = to_bf16x8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
-    sbv[1] = to_bf16x8(dsv[8], dsv[9], dsv[10], dsv[11], dsv[12], dsv[13], dsv[14], dsv[15]);
-  };
-  // dV^T += dO^T P and dK^T += Q^T dS for one sub-block (scale at the end)
-  auto accumulate = [&] __device__ (const char* qs, const char* ds, const bf16x8* pb, const bf16x8* sbv) {
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      dv[ct] = mfma32(toff.read_tr(ds, 0, ct), pb[0], dv[ct]);
-      dv[ct] = mfma32(toff.read_tr(ds, 1, ct), pb[1], dv[ct]);
-      dk[ct] = mfma32(toff.read_tr(qs, 0, ct), sbv[0], dk[ct]);
-      dk[ct] = mfma32(toff.read_tr(qs, 1, ct), sbv[1], dk[ct]);
-    }
-  };
-
-  // One 64-query tile as a software pipeline over its two 32-query
-  // sub-blocks, in one scheduling region: products(0); products(1) with
-  // grads(0) on the VALU; accumulate(0) with grads(1); accumulate(1).
-  auto compute = [&] __device__ (auto edge_c, const char* qt, const char* dt, const float* lt,
-                                 const float* et, int q0) {
-    const char* qs1 = qt + 32 * PITCH;
-    const char* ds1 = dt + 32 * PITCH;
-    f32x16 S0, dP0, S1, dP1;
-    bf16x8 pb0[2], sv0[2], pb1[2], sv1[2];
-    // phase A: products(0), operand reads three k-steps ahead
-    products(qt, dt, S0, dP0);
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 3);
-#pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 3);
-      if (kc + 3 < NKC) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 3);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // phase B: products(1) on the matrix pipe, grads(0) on the VALU
-    products(qs1, ds1, S1, dP1);
-    grads(edge_c, S0, dP0, lt, et, 0, q0, pb0, sv0);
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 4);
-#pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 4);
-      __builtin_amdgcn_sched_group_barrier(kSchedValu, 40 / NKC, 4);
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 4);
-      __builtin_amdgcn_sched_group_barrier(kSchedValu, 40 / NKC, 4);
-      if (kc + 3 < NKC) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 4);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // phase C: accumulate(0) on the matrix pipe, grads(1) on the VALU
-    accumulate(qt, dt, pb0, sv0);
-    grads(edge_c, S1, dP1, lt, et, 1, q0, pb1, sv1);
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 12, 5);
-#pragma unroll
-    for (int m = 0; m < 4 * NCT; ++m) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 5);
-      __builtin_amdgcn_sched_group_barrier(kSchedValu, 80 / (4 * NCT), 5);
-      if (m + 6 < 4 * NCT) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 5);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // phase D: accumulate(1)
-    accumulate(qs1, ds1, pb1, sv1);
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 12, 6);
-#pragma unroll
-    for (int m = 0; m < 4 * NCT; ++m) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 6);
-      if (m + 6 < 4 * NCT) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 6);
-    }
-  };
-
-  // Sub-blocks one after the other (d=64, two waves per SIMD).
+  // The tile's two 32-query sub-blocks, one after the other.
   auto compute_seq = [&] __device__ (const char* qt, const char* dt, const float* lt, const float* et, int q0) {
 #pragma unroll
     for (int sb = 0; sb < BQ / 32; ++sb) {
@@ -409,17 +285,7 @@ __global__ __launch_bounds__(256, DkdvTile<D>::MIN_WG) void bwd_dkdv_kernel(BwdA
         nv = load_vec(q1);
       }
       const int q0 = tile_of(t) * BQ;
-      if constexpr (T::PIPE) {
-        // masking only where the tile crosses the diagonal or the sequence end
-        if (kw0 < N && !(CAUSAL && q0 + BQ - 1 < kw0)) {
-          if ((CAUSAL && q0 < kw0 + 31) || (q0 + BQ > N))
-            compute(std::true_type{}, qc, dc, lc, ec, q0);
-          else
-            compute(std::false_type{}, qc, dc, lc, ec, q0);
-        }
-      } else {
-        if (kw0 < N) compute_seq(qc, dc, lc, ec, q0);
-      }
+      if (kw0 < N) compute_seq(qc, dc, lc, ec, q0);
       if (t + 1 < ntiles) store_vec(ln, en, nv);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
@@ -447,6 +313,286 @@ __global__ __launch_bounds__(256, DkdvTile<D>::MIN_WG) void bwd_dkdv_kernel(BwdA
         const float vs = DROP ? a.drop.keep_scale : 1.f;  // dV = (P o Z)^T dO / (1 - p)
         pv[0] = f32x4{dv[ct][r0] * vs, dv[ct][r0 + 1] * vs, dv[ct][r0 + 2] * vs, dv[ct][r0 + 3] * vs};
         pv[1] = f32x4{dv[ct][r0 + 4] * vs, dv[ct][r0 + 5] * vs, dv[ct][r0 + 6] * vs, dv[ct][r0 + 7] * vs};
+      }
+  }
+}
+
+// ---- dK, dV with a wave pair per 32 keys --------------------------------------
+// A wave issues an LDS read only every ~23-31 cycles whatever its width
+// (measured on gfx950), and the kernel above issues 1.5 of them per MFMA; at
+// d = 128 it runs one wave per SIMD and is bound by that issue rate.  Here
+// the work of each 32-key group is split between two waves on one SIMD:
+//   the P-wave holds K, computes S = Q K^T and P, hands P to its partner
+//   through LDS and accumulates dV^T += dO^T P;
+//   the dS-wave holds V, computes dP = dO V^T, takes P and forms
+//   dS = P o (dP - D), and accumulates dK^T += Q^T dS.
+// Each wave needs about half the registers of the single-wave kernel, so two
+// share a SIMD and the LDS reads of one overlap the MFMAs of the other.  P
+// crosses in fp32 with the dropout decision in its sign bit, so every value
+// is computed exactly as in the single-wave kernel.
+template <int D>
+struct DkdvPairTile {
+  static constexpr int NW = 8;
+  static constexpr int NT = 64 * NW;
+  static constexpr int NPAIR = NW / 2;
+  static constexpr int BK = 32 * NPAIR;  // 128 keys per workgroup
+  static constexpr int BQ = 64;          // queries per tile
+  static constexpr int PITCH = 2 * D;
+  static constexpr int T_BYTES = BQ * PITCH;
+  static constexpr int P_BYTES = BQ * 32 * 4;  // one pair's P of a tile, fp32
+  static constexpr int LIST_CAP = 1024;
+};
+
+// Workgroup barrier for LDS written by the waves themselves: the
+// direct-to-LDS tile copies still in flight (vmcnt) are not waited for.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int D, bool CAUSAL, bool MASK, bool DROP>
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
+  using T = DkdvPairTile<D>;
+  constexpr int NT = T::NT, BQ = T::BQ, BK = T::BK, PITCH = T::PITCH;
+  constexpr int NKC = D / 16, NCT = D / 32;
+  constexpr int TPB = 128 / BQ;  // query tiles per mask block
+  __shared__ __attribute__((aligned(1024))) char qb0[T::T_BYTES];
+  __shared__ __attribute__((aligned(1024))) char qb1[T::T_BYTES];
+  __shared__ __attribute__((aligned(1024))) char db0[T::T_BYTES];
+  __shared__ __attribute__((aligned(1024))) char db1[T::T_BYTES];
+  __shared__ __attribute__((aligned(1024))) char pbuf[T::NPAIR * T::P_BYTES];
+  __shared__ __attribute__((aligned(16))) float lb0[BQ], lb1[BQ], eb0[BQ], eb1[BQ];
+  __shared__ int blist[MASK ? T::LIST_CAP : 1];
+  __shared__ int wcount[T::NW];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = w & (T::NPAIR - 1);
+  const bool ds_wave = w >= T::NPAIR;  // waves w and w + 4 share a SIMD
+  const int h = lane >> 5, li = lane & 31;
+  const int g = xcd_remap(blockIdx.x, a.total);
+  const int bh = g / a.ntile;
+  const int kt = g - bh * a.ntile;
+  const int N = a.N;
+  const size_t head = (size_t)bh * N * D;
+  const int k0 = kt * BK;
+  const int kw0 = k0 + 32 * pair;
+  const int kj = kw0 + li;  // this lane's key
+
+  // B operand rows: K (P-wave) or V (dS-wave), row kj, columns 16kc+8h..+7
+  bf16x8 bop[NKC];
+  {
+    const __bf16* src = (ds_wave ? a.v : a.k) + head + (size_t)kj * D;
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      u32x4 x = u32x4{0u, 0u, 0u, 0u};
+      if (kj < N) x = gload16(src + 16 * kc + 8 * h);
+      bop[kc] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+  f32x16 acc[NCT];  // dV^T (P-wave) or dK^T (dS-wave)
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) acc[ct] = f32x16{};
+
+  const __bf16* Qh = a.q + head;
+  const __bf16* dOh = a.dout + head;
+  const float* Lh = a.lse + (size_t)bh * N;
+  const float* Dh = a.Dw + (size_t)bh * N;
+  const float c = a.c;
+  TileOffsets<D> toff;
+  toff.init(lane);
+  TileCopy<BQ, D, NT> cp;
+  cp.init(w, lane);
+  // this lane's 16-byte slots of the pair's P: + 1024 * (4 * sb + j)
+  char* const pslot = pbuf + pair * T::P_BYTES + 16 * lane;
+
+  auto load_vec = [&] __device__ (int q0) -> float {
+    const int i = q0 + lane;
+    if (w == 0) {
+      float l = (i < N) ? Lh[i] * kLog2e : 0.f;
+      return (l == -INFINITY) ? INFINITY : l;
+    }
+    return (w == 1 && i < N) ? Dh[i] : 0.f;
+  };
+  auto store_vec = [&] __device__ (float* lb, float* eb, float x) {
+    if (w == 0) lb[lane] = x;
+    else if (w == 1) eb[lane] = x;
+  };
+
+  // Phase 1: X = S (P-wave, rows of Q) or dP (dS-wave, rows of dO) for the
+  // two 32-query sub-blocks; the P-wave turns S into P, keeps it as bf16 B
+  // operands and writes it (fp32) for its partner.
+  auto phase1 = [&] __device__ (auto role_c, auto edge_c, const char* qt, const char* dt, const float* lt,
+                                int q0, f32x16* X, bf16x8* pb) __attribute__((always_inline)) {
+    constexpr bool DS = decltype(role_c)::value;
+    constexpr bool EDGE = decltype(edge_c)::value;
+    const char* src = DS ? dt : qt;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      bf16x8 av[NKC];
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) av[kc] = lds_read16(src + 32 * sb * PITCH + toff.rows[kc]);
+      X[sb] = f32x16{};
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) X[sb] = mfma32(av[kc], bop[kc], X[sb]);
+    }
+    if constexpr (DS) return;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      const int qs0 = q0 + 32 * sb;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const f32x4 l0 = *reinterpret_cast<const f32x4*>(lt + 32 * sb + 16 * hf + 8 * h);
+        const f32x4 l1 = *reinterpret_cast<const f32x4*>(lt + 32 * sb + 16 * hf + 8 * h + 4);
+        uint32_t kbits = 0xFFu;  // keep bits of rows 8hf .. 8hf+7
+        if constexpr (DROP) {
+          const int i0 = qs0 + 16 * hf + 8 * h;
+          kbits = keep4_keylane(a.drop, bh, i0, kj, lane) | (keep4_keylane(a.drop, bh, i0 + 4, kj, lane) << 4);
+        }
+        float p[8], x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = 8 * hf + e;
+          const float lv = e < 4 ? l0[e] : l1[e - 4];
+          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(X[sb][r], c, -lv));
+          if (EDGE) {
+            const int qq = qs0 + acc_row(r, h);
+            if ((CAUSAL && kj > qq) || qq >= N) pv = 0.f;
+          }
+          if constexpr (DROP) {
+            const bool kept = (kbits >> e) & 1u;
+            p[e] = kept ? pv : 0.f;
+            x[e] = kept ? pv : -pv;
+          } else {
+            p[e] = pv;
+            x[e] = pv;
+          }
+        }
+        pb[2 * sb + hf] = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+        f32x4* dst = reinterpret_cast<f32x4*>(pslot + 1024 * (4 * sb + 2 * hf));
+        dst[0] = f32x4{x[0], x[1], x[2], x[3]};
+        *reinterpret_cast<f32x4*>(pslot + 1024 * (4 * sb + 2 * hf + 1)) = f32x4{x[4], x[5], x[6], x[7]};
+      }
+    }
+  };
+
+  // Phase 2: the dS-wave forms dS = P o (dP - D) from its partner's P; both
+  // accumulate over the tile's queries through transposed reads: dV^T +=
+  // dO^T P (P-wave), dK^T += Q^T dS (dS-wave).
+  auto phase2 = [&] __device__ (auto role_c, const char* qt, const char* dt, const float* et, const f32x16* X,
+                                bf16x8* pb) __attribute__((always_inline)) {
+    constexpr bool DS = decltype(role_c)::value;
+    if constexpr (DS) {
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const f32x4 e0 = *reinterpret_cast<const f32x4*>(et + 32 * sb + 16 * hf + 8 * h);
+          const f32x4 e1 = *reinterpret_cast<const f32x4*>(et + 32 * sb + 16 * hf + 8 * h + 4);
+          const f32x4 x0 = *reinterpret_cast<const f32x4*>(pslot + 1024 * (4 * sb + 2 * hf));
+          const f32x4 x1 = *reinterpret_cast<const f32x4*>(pslot + 1024 * (4 * sb + 2 * hf + 1));
+          float dsv[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int r = 8 * hf + e;
+            const float x = e < 4 ? x0[e] : x1[e - 4];
+            const float dvv = e < 4 ? e0[e] : e1[e - 4];
+            if constexpr (DROP) {
+              const bool kept = (__float_as_uint(x) >> 31) == 0u;
+              const float pv = __builtin_fabsf(x);
+              dsv[e] = pv * ((kept ? X[sb][r] * a.drop.keep_scale : 0.f) - dvv);
+            } else {
+              dsv[e] = x * (X[sb][r] - dvv);
+            }
+          }
+          pb[2 * sb + hf] = to_bf16x8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
+        }
+    }
+    const char* src = DS ? qt : dt;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        acc[ct] = mfma32(toff.read_tr(src + 32 * sb * PITCH, 0, ct), pb[2 * sb], acc[ct]);
+        acc[ct] = mfma32(toff.read_tr(src + 32 * sb * PITCH, 1, ct), pb[2 * sb + 1], acc[ct]);
+      }
+  };
+
+  // the whole tile loop in one copy per role, so that each role's
+  // registers are allocated for that role alone (the barriers match)
+  auto run = [&] __device__ (auto role_c) __attribute__((always_inline)) {
+  const int kb = k0 >> 7;  // mask column (BK == 128)
+  const int nqt_all = (N + BQ - 1) / BQ;
+  const int qb_lo = CAUSAL ? kb : 0;
+  for (int cb0 = qb_lo; cb0 < (MASK ? a.nb : qb_lo + 1); cb0 += T::LIST_CAP) {
+    int ntiles, first = 0;
+    if (!MASK) {
+      first = CAUSAL ? k0 / BQ : 0;
+      ntiles = nqt_all - first;
+    } else {
+      const int cb1 = min(a.nb, cb0 + T::LIST_CAP);
+      const int cnt = compact_mask_run<NT>(a.mask, (size_t)kb, (size_t)a.nb, cb0, cb1, blist, wcount);
+      ntiles = cnt * TPB;
+      if (cnt > 0 && blist[cnt - 1] * TPB + TPB > nqt_all) ntiles -= blist[cnt - 1] * TPB + TPB - nqt_all;
+    }
+    auto tile_of = [&] __device__ (int t) -> int { return MASK ? blist[t / TPB] * TPB + (t % TPB) : first + t; };
+    if (ntiles == 0) continue;
+
+    {
+      const int q0 = tile_of(0) * BQ;
+      cp.issue(qb0, Qh, q0, N, w);
+      cp.issue(db0, dOh, q0, N, w);
+      store_vec(lb0, eb0, load_vec(q0));
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    auto step = [&] __device__ (int t, const char* qc, const char* dc, const float* lc, const float* ec,
+                                char* qn, char* dn, float* ln, float* en) __attribute__((always_inline)) {
+      float nv = 0.f;
+      if (t + 1 < ntiles) {
+        const int q1 = tile_of(t + 1) * BQ;
+        cp.issue(qn, Qh, q1, N, w);
+        cp.issue(dn, dOh, q1, N, w);
+        nv = load_vec(q1);
+      }
+      const int q0 = tile_of(t) * BQ;
+      // the pair has work unless its keys are past the end or follow every query
+      const bool live = kw0 < N && !(CAUSAL && q0 + BQ - 1 < kw0);
+      f32x16 X[2];
+      bf16x8 pb[4];
+      if (live) {
+        if ((CAUSAL && q0 < kw0 + 31) || (q0 + BQ > N))
+          phase1(role_c, std::true_type{}, qc, dc, lc, q0, X, pb);
+        else
+          phase1(role_c, std::false_type{}, qc, dc, lc, q0, X, pb);
+      }
+      lds_barrier();  // P of the tile is in LDS
+      if (live) phase2(role_c, qc, dc, ec, X, pb);
+      if (t + 1 < ntiles) store_vec(ln, en, nv);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();  // next tile landed; this tile's buffers and P are free
+    };
+    for (int t = 0; t < ntiles; t += 2) {
+      step(t, qb0, db0, lb0, eb0, qb1, db1, lb1, eb1);
+      if (t + 1 < ntiles) step(t + 1, qb1, db1, lb1, eb1, qb0, db0, lb0, eb0);
+    }
+  }
+  };
+  if (ds_wave) run(std::true_type{});
+  else run(std::false_type{});
+
+  if (kj < N) {
+    // dK = scale * dS^T Q; dV = (P o Z)^T dO / (1 - p) under dropout
+    float* row = (ds_wave ? a.dk : a.dv) + head + (size_t)kj * D;
+    const float sc = ds_wave ? a.scale : (DROP ? a.drop.keep_scale : 1.f);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int col = 32 * ct + 16 * hh + 8 * h;
+        const int r0 = 8 * hh;
+        f32x4* pr = reinterpret_cast<f32x4*>(row + col);
+        pr[0] = f32x4{acc[ct][r0] * sc, acc[ct][r0 + 1] * sc, acc[ct][r0 + 2] * sc, acc[ct][r0 + 3] * sc};
+        pr[1] = f32x4{acc[ct][r0 + 4] * sc, acc[ct][r0 + 5] * sc, acc[ct][r0 + 6] * sc, acc[ct][r0 + 7] * sc};
       }
   }
 }
