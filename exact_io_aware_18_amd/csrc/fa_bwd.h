@@ -400,8 +400,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
   const float c = a.c;
   TileOffsets<D> toff;
   toff.init(lane);
-  TileCopy<BQ, D, NT> cp;
-  cp.init(w, lane);
+  // the four dS-waves copy the Q tiles, the four P-waves the dO tiles
+  TileCopy<BQ, D, NT / 2> cp;
+  cp.init(pair, lane);
   // this lane's 16-byte slots of the pair's P: + 1024 * (4 * sb + j)
   char* const pslot = pbuf + pair * T::P_BYTES + 16 * lane;
 
@@ -422,7 +423,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
   // two 32-query sub-blocks; the P-wave turns S into P, keeps it as bf16 B
   // operands and writes it (fp32) for its partner.
   auto phase1 = [&] __device__ (auto role_c, auto edge_c, const char* qt, const char* dt, const float* lt,
-                                int q0, f32x16* X, bf16x8* pb) __attribute__((always_inline)) {
+                                const float* et, int q0, f32x16* X, bf16x8* pb) __attribute__((always_inline)) {
     constexpr bool DS = decltype(role_c)::value;
     constexpr bool EDGE = decltype(edge_c)::value;
     const char* src = DS ? dt : qt;
@@ -435,7 +436,21 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) X[sb] = mfma32(av[kc], bop[kc], X[sb]);
     }
-    if constexpr (DS) return;
+    if constexpr (DS) {
+      // dP - D here, where the dS-wave would otherwise wait for P
+      if constexpr (!DROP) {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            const f32x4 e0 = *reinterpret_cast<const f32x4*>(et + 32 * sb + 16 * hf + 8 * h);
+            const f32x4 e1 = *reinterpret_cast<const f32x4*>(et + 32 * sb + 16 * hf + 8 * h + 4);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) X[sb][8 * hf + e] -= e < 4 ? e0[e] : e1[e - 4];
+          }
+      }
+      return;
+    }
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
       const int qs0 = q0 + 32 * sb;
@@ -486,23 +501,23 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-          const f32x4 e0 = *reinterpret_cast<const f32x4*>(et + 32 * sb + 16 * hf + 8 * h);
-          const f32x4 e1 = *reinterpret_cast<const f32x4*>(et + 32 * sb + 16 * hf + 8 * h + 4);
           const f32x4 x0 = *reinterpret_cast<const f32x4*>(pslot + 1024 * (4 * sb + 2 * hf));
           const f32x4 x1 = *reinterpret_cast<const f32x4*>(pslot + 1024 * (4 * sb + 2 * hf + 1));
           float dsv[8];
+          if constexpr (DROP) {
+            const f32x4 e0 = *reinterpret_cast<const f32x4*>(et + 32 * sb + 16 * hf + 8 * h);
+            const f32x4 e1 = *reinterpret_cast<const f32x4*>(et + 32 * sb + 16 * hf + 8 * h + 4);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int r = 8 * hf + e;
-            const float x = e < 4 ? x0[e] : x1[e - 4];
-            const float dvv = e < 4 ? e0[e] : e1[e - 4];
-            if constexpr (DROP) {
+            for (int e = 0; e < 8; ++e) {
+              const int r = 8 * hf + e;
+              const float x = e < 4 ? x0[e] : x1[e - 4];
+              const float dvv = e < 4 ? e0[e] : e1[e - 4];
               const bool kept = (__float_as_uint(x) >> 31) == 0u;
-              const float pv = __builtin_fabsf(x);
-              dsv[e] = pv * ((kept ? X[sb][r] * a.drop.keep_scale : 0.f) - dvv);
-            } else {
-              dsv[e] = x * (X[sb][r] - dvv);
+              dsv[e] = __builtin_fabsf(x) * ((kept ? X[sb][r] * a.drop.keep_scale : 0.f) - dvv);
             }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dsv[e] = (e < 4 ? x0[e] : x1[e - 4]) * X[sb][8 * hf + e];  // X = dP - D
           }
           pb[2 * sb + hf] = to_bf16x8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
         }
@@ -539,19 +554,19 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
 
     {
       const int q0 = tile_of(0) * BQ;
-      cp.issue(qb0, Qh, q0, N, w);
-      cp.issue(db0, dOh, q0, N, w);
+      if constexpr (decltype(role_c)::value) cp.issue(qb0, Qh, q0, N, pair);
+      else cp.issue(db0, dOh, q0, N, pair);
       store_vec(lb0, eb0, load_vec(q0));
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     auto step = [&] __device__ (int t, const char* qc, const char* dc, const float* lc, const float* ec,
                                 char* qn, char* dn, float* ln, float* en) __attribute__((always_inline)) {
+      constexpr bool DS = decltype(role_c)::value;
       float nv = 0.f;
+      const int q1 = (t + 1 < ntiles) ? tile_of(t + 1) * BQ : 0;
       if (t + 1 < ntiles) {
-        const int q1 = tile_of(t + 1) * BQ;
-        cp.issue(qn, Qh, q1, N, w);
-        cp.issue(dn, dOh, q1, N, w);
+        if constexpr (DS) cp.issue(qn, Qh, q1, N, pair);  // the dS-wave waits for P in phase 1 anyway
         nv = load_vec(q1);
       }
       const int q0 = tile_of(t) * BQ;
@@ -561,11 +576,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
       bf16x8 pb[4];
       if (live) {
         if ((CAUSAL && q0 < kw0 + 31) || (q0 + BQ > N))
-          phase1(role_c, std::true_type{}, qc, dc, lc, q0, X, pb);
+          phase1(role_c, std::true_type{}, qc, dc, lc, ec, q0, X, pb);
         else
-          phase1(role_c, std::false_type{}, qc, dc, lc, q0, X, pb);
+          phase1(role_c, std::false_type{}, qc, dc, lc, ec, q0, X, pb);
       }
       lds_barrier();  // P of the tile is in LDS
+      if constexpr (!DS) {  // and the P-wave has the shorter phase 2
+        if (t + 1 < ntiles) cp.issue(dn, dOh, q1, N, pair);
+      }
       if (live) phase2(role_c, qc, dc, ec, X, pb);
       if (t + 1 < ntiles) store_vec(ln, en, nv);
       __builtin_amdgcn_s_waitcnt(0);
