@@ -523,13 +523,23 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
         }
     }
     const char* src = DS ? qt : dt;
+    // MFMA m = 2 NCT sb + 2 ct + hf in the order of the sums; its transposed
+    // operand is read three MFMAs ahead into a ring of four, one scheduling
+    // step per MFMA, so each wait covers exactly the operand it needs
+    constexpr int NM = 4 * NCT;
+    auto opnd = [&] __device__ (int m) -> bf16x8 {
+      return toff.read_tr(src + 32 * (m / (2 * NCT)) * PITCH, m & 1, (m >> 1) % NCT);
+    };
+    bf16x8 ring[4];
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
+    for (int m = 0; m < 3; ++m) ring[m] = opnd(m);
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        acc[ct] = mfma32(toff.read_tr(src + 32 * sb * PITCH, 0, ct), pb[2 * sb], acc[ct]);
-        acc[ct] = mfma32(toff.read_tr(src + 32 * sb * PITCH, 1, ct), pb[2 * sb + 1], acc[ct]);
-      }
+    for (int m = 0; m < NM; ++m) {
+      if (m + 3 < NM) ring[(m + 3) & 3] = opnd(m + 3);
+      const int ct = (m >> 1) % NCT;
+      acc[ct] = mfma32(ring[m & 3], pb[2 * (m / (2 * NCT)) + (m & 1)], acc[ct]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   // the whole tile loop in one copy per role, so that each role's
