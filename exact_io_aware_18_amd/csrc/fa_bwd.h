@@ -153,19 +153,21 @@ __global__ __launch_bounds__(256, DkdvTile<D>::MIN_WG) void bwd_dkdv_kernel(BwdA
   TileCopy<BQ, D, NT> cp;  // Q and dO tiles have the same shape
   cp.init(w, lane);
 
-  // lse*log2(e) (wave 0) and D (wave 1) of the tile's queries go through
-  // registers: an empty row's lse = -inf becomes +inf so that P = 0.
+  // raw lse (wave 0) or D (wave 1) of query q0 + lane, loaded a step ahead
+  // and converted only when stored, so that nothing waits for the load early
   auto load_vec = [&] __device__ (int q0) -> float {
     const int i = q0 + lane;
-    if (w == 0) {
-      float l = (i < N) ? Lh[i] * kLog2e : 0.f;
-      return (l == -INFINITY) ? INFINITY : l;
-    }
-    return (w == 1 && i < N) ? Dh[i] : 0.f;
+    float x = 0.f;
+    if (w < 2 && i < N) x = (w == 0 ? Lh : Dh)[i];
+    return x;
   };
   auto store_vec = [&] __device__ (float* lb, float* eb, float x) {
-    if (w == 0) lb[lane] = x;
-    else if (w == 1) eb[lane] = x;
+    if (w == 0) {
+      const float l = x * kLog2e;
+      lb[lane] = (l == -INFINITY) ? INFINITY : l;  // empty row: P = 0
+    } else if (w == 1) {
+      eb[lane] = x;
+    }
   };
 
   // The tile's two 32-query sub-blocks, one after the other.
@@ -406,17 +408,21 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
   // this lane's 16-byte slots of the pair's P: + 1024 * (4 * sb + j)
   char* const pslot = pbuf + pair * T::P_BYTES + 16 * lane;
 
+  // raw lse (wave 0) or D (wave 1) of query q0 + lane, loaded a step ahead
+  // and converted only when stored, so that nothing waits for the load early
   auto load_vec = [&] __device__ (int q0) -> float {
     const int i = q0 + lane;
-    if (w == 0) {
-      float l = (i < N) ? Lh[i] * kLog2e : 0.f;
-      return (l == -INFINITY) ? INFINITY : l;
-    }
-    return (w == 1 && i < N) ? Dh[i] : 0.f;
+    float x = 0.f;
+    if (w < 2 && i < N) x = (w == 0 ? Lh : Dh)[i];
+    return x;
   };
   auto store_vec = [&] __device__ (float* lb, float* eb, float x) {
-    if (w == 0) lb[lane] = x;
-    else if (w == 1) eb[lane] = x;
+    if (w == 0) {
+      const float l = x * kLog2e;
+      lb[lane] = (l == -INFINITY) ? INFINITY : l;  // empty row: P = 0
+    } else if (w == 1) {
+      eb[lane] = x;
+    }
   };
 
   // Phase 1: X = S (P-wave, rows of Q) or dP (dS-wave, rows of dO) for the

@@ -113,9 +113,20 @@ __device__ __forceinline__ int xcd_remap(int g, int total) {
 }
 
 // 16-byte direct-to-LDS copy (global_load_lds_dwordx4): lane l of the wave
-// writes its 16 bytes at lds + 16*l; lds must be wave-uniform.
-__device__ __forceinline__ void lds_dma16(const void* src, char* lds) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+// writes its 16 bytes at lds + 16*l; lds must be wave-uniform.  Issued
+// through inline assembly so that the compiler does not track it: while it
+// tracks a direct-to-LDS copy in flight, it turns every LDS-read wait into a
+// full lgkmcnt(0) and every workgroup barrier into a wait for the copy.
+// Users therefore wait for these copies themselves (s_waitcnt vmcnt(0), then
+// a barrier) before any wave reads the destination; the compiler's own vmcnt
+// waits for other loads can only become longer (completions are in order),
+// never too short.
+__device__ __forceinline__ void lds_dma16_untracked(const void* src, char* lds) {
+  const uint32_t m = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(m)
+               : "memory", "m0");
 }
 
 // Direct-to-LDS copy of ROWS consecutive rows of a [N][D] bf16 matrix into
@@ -142,18 +153,20 @@ struct TileCopy {
     }
   }
   // rows [row0, row0 + ROWS) of src; rows past N re-read row N-1 (finite
-  // data that the callers mask)
+  // data that the callers mask).  The copies are untracked: the caller waits
+  // (s_waitcnt vmcnt(0) and a barrier) before the tile is read.
   __device__ __forceinline__ void issue(char* lds_tile, const __bf16* src, int row0, int N, int w) const {
     const char* base = reinterpret_cast<const char*>(src + (size_t)row0 * D);
+    auto dma = [&](const char* g, char* l) { lds_dma16_untracked(g, l); };
     if (row0 + ROWS <= N) {
 #pragma unroll
-      for (int e = 0; e < ROUNDS; ++e) lds_dma16(base + off[e], lds_tile + (e * NW + w) * 1024);
+      for (int e = 0; e < ROUNDS; ++e) dma(base + off[e], lds_tile + (e * NW + w) * 1024);
     } else {
       const uint32_t last = (uint32_t)((N - 1 - row0) * PITCH);  // byte offset of row N-1
 #pragma unroll
       for (int e = 0; e < ROUNDS; ++e) {
         const uint32_t o = (row0 + row[e] < N) ? off[e] : last + (off[e] - (uint32_t)(row[e] * PITCH));
-        lds_dma16(base + o, lds_tile + (e * NW + w) * 1024);
+        dma(base + o, lds_tile + (e * NW + w) * 1024);
       }
     }
   }
