@@ -704,23 +704,24 @@ __global__ __launch_bounds__(256, DqTile<D>::MIN_WG) void bwd_dq_kernel(BwdArgs 
     bf16x8 dsb[4];
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
-      bf16x8 ak[NKC], av[NKC];
-#pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) {
-        ak[kc] = lds_read16(kt + toff.rows[kc] + 32 * t2 * PITCH);
-        av[kc] = lds_read16(vt + toff.rows[kc] + 32 * t2 * PITCH);
-      }
+      // S^T and dP^T: MFMA m takes K (m even) or V (m odd) rows of k-step
+      // m/2, read three MFMAs ahead into a ring of four, one scheduling step
+      // per MFMA, so each wait covers exactly the operand it needs
+      auto rowop = [&] __device__ (int m) -> bf16x8 {
+        return lds_read16(((m & 1) ? vt : kt) + toff.rows[m >> 1] + 32 * t2 * PITCH);
+      };
       f32x16 S = f32x16{}, dP = f32x16{};
+      {
+        bf16x8 ring[4];
 #pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) {
-        S = mfma32(ak[kc], qf[kc], S);
-        dP = mfma32(av[kc], df[kc], dP);
-      }
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 5);
+        for (int m = 0; m < 3; ++m) ring[m] = rowop(m);
 #pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 5);
-        if (kc + 3 < NKC) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 5);
+        for (int m = 0; m < 2 * NKC; ++m) {
+          if (m + 3 < 2 * NKC) ring[(m + 3) & 3] = rowop(m + 3);
+          if (m & 1) dP = mfma32(ring[m & 3], df[m >> 1], dP);
+          else S = mfma32(ring[m & 3], qf[m >> 1], S);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
       float dsv[16];
       uint32_t kbits = 0xFFFFu;  // keep bits of rows 0..15 (keys k0 + 32 t2 + acc_row(r, h))
@@ -747,15 +748,19 @@ __global__ __launch_bounds__(256, DqTile<D>::MIN_WG) void bwd_dq_kernel(BwdArgs 
       dsb[2 * t2 + 1] = to_bf16x8(dsv[8], dsv[9], dsv[10], dsv[11], dsv[12], dsv[13], dsv[14], dsv[15]);
     }
     __builtin_amdgcn_sched_barrier(0);
+    // dQ^T += K^T dS^T: MFMA m = (BC/16) ct + kc, transposed K operands
+    // three MFMAs ahead as above
+    {
+      constexpr int KS = BC / 16, NM = NCT * KS;
+      bf16x8 ring[4];
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
+      for (int m = 0; m < 3; ++m) ring[m] = toff.read_tr(kt, m % KS, m / KS);
 #pragma unroll
-      for (int kc = 0; kc < BC / 16; ++kc) dq[ct] = mfma32(toff.read_tr(kt, kc, ct), dsb[kc], dq[ct]);
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 7);
-#pragma unroll
-    for (int m = 0; m < NCT * BC / 16; ++m) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 7);
-      if (m + 2 < NCT * BC / 16) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 7);
+      for (int m = 0; m < NM; ++m) {
+        if (m + 3 < NM) ring[(m + 3) & 3] = toff.read_tr(kt, (m + 3) % KS, (m + 3) / KS);
+        dq[m / KS] = mfma32(ring[m & 3], dsb[m % KS], dq[m / KS]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
 
