@@ -178,23 +178,22 @@ __global__ __launch_bounds__(256, DkdvTile<D>::MIN_WG) void bwd_dkdv_kernel(BwdA
       if (CAUSAL && qs0 + 31 < kw0) continue;  // every query precedes every key
       const char* qs = qt + 32 * sb * PITCH;
       const char* ds = dt + 32 * sb * PITCH;
-      bf16x8 aq[NKC], ad[NKC];
-#pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) {
-        aq[kc] = lds_read16(qs + toff.rows[kc]);
-        ad[kc] = lds_read16(ds + toff.rows[kc]);
-      }
+      // S = Q K^T and dP = dO V^T: MFMA m takes Q (m even) or dO (m odd)
+      // rows of k-step m/2, read three MFMAs ahead into a ring of four, one
+      // scheduling step per MFMA, so each wait covers exactly its operand
+      auto rowop = [&] __device__ (int m) -> bf16x8 { return lds_read16(((m & 1) ? ds : qs) + toff.rows[m >> 1]); };
       f32x16 S = f32x16{}, dP = f32x16{};
+      {
+        bf16x8 ring[4];
 #pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) {
-        S = mfma32(aq[kc], kf[kc], S);
-        dP = mfma32(ad[kc], vf[kc], dP);
-      }
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 3);
+        for (int m = 0; m < 3; ++m) ring[m] = rowop(m);
 #pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 3);
-        if (kc + 3 < NKC) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 3);
+        for (int m = 0; m < 2 * NKC; ++m) {
+          if (m + 3 < 2 * NKC) ring[(m + 3) & 3] = rowop(m + 3);
+          if (m & 1) dP = mfma32(ring[m & 3], vf[m >> 1], dP);
+          else S = mfma32(ring[m & 3], kf[m >> 1], S);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
       // lane's queries: 32sb + 16*hf + 8h + e, e = 0..7
       const bool edge = (CAUSAL && qs0 < kw0 + 31) || (qs0 + 32 > N);
@@ -235,19 +234,22 @@ __global__ __launch_bounds__(256, DkdvTile<D>::MIN_WG) void bwd_dkdv_kernel(BwdA
       const bf16x8 sb0 = to_bf16x8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
       const bf16x8 sb1 = to_bf16x8(dsv[8], dsv[9], dsv[10], dsv[11], dsv[12], dsv[13], dsv[14], dsv[15]);
       __builtin_amdgcn_sched_barrier(0);
-      // dV^T += dO^T P and dK^T += Q^T dS (scale applied at the end)
+      // dV^T += dO^T P and dK^T += Q^T dS (scale applied at the end): MFMA
+      // m = 4 ct + j, j = dV k-step 0, 1, dK k-step 0, 1; transposed
+      // operands in a ring as above
+      auto trop = [&] __device__ (int m) -> bf16x8 { return toff.read_tr((m & 2) ? qs : ds, m & 1, m >> 2); };
+      {
+        bf16x8 ring[4];
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        dv[ct] = mfma32(toff.read_tr(ds, 0, ct), pb0, dv[ct]);
-        dv[ct] = mfma32(toff.read_tr(ds, 1, ct), pb1, dv[ct]);
-        dk[ct] = mfma32(toff.read_tr(qs, 0, ct), sb0, dk[ct]);
-        dk[ct] = mfma32(toff.read_tr(qs, 1, ct), sb1, dk[ct]);
-      }
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 4);
+        for (int m = 0; m < 3; ++m) ring[m] = trop(m);
 #pragma unroll
-      for (int m = 0; m < 4 * NCT; ++m) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 4);
-        if (m + 2 < 4 * NCT) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 4);
+        for (int m = 0; m < 4 * NCT; ++m) {
+          if (m + 3 < 4 * NCT) ring[(m + 3) & 3] = trop(m + 3);
+          const int ct = m >> 2;
+          if (m & 2) dk[ct] = mfma32(ring[m & 3], (m & 1) ? sb1 : sb0, dk[ct]);
+          else dv[ct] = mfma32(ring[m & 3], (m & 1) ? pb1 : pb0, dv[ct]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
   };
