@@ -75,33 +75,52 @@ void launch_fwd_t(const fa::FwdArgs& a, int grid, hipStream_t s) {
   hipLaunchKernelGGL((fa::fwd_bf16_kernel<D, CAUSAL, MASK, DROP>), dim3(grid), dim3(256), 0, s, a);
 }
 
-template <int D, bool CAUSAL, bool DROP>
+template <int D, int G, bool CAUSAL, bool DROP>
 void launch_fwd_pp(fa::FwdArgs a, int BH, hipStream_t s) {
-  a.nqt = (a.N + fa::FwdPPTile<D>::BR - 1) / fa::FwdPPTile<D>::BR;
+  using T = fa::FwdPPTile<D, G>;
+  a.nqt = (a.N + T::BR - 1) / T::BR;
   a.total = BH * a.nqt;
-  hipLaunchKernelGGL((fa::fwd_pp_kernel<D, CAUSAL, DROP>), dim3(a.total), dim3(fa::FwdPPTile<D>::NT), 0, s, a);
+  hipLaunchKernelGGL((fa::fwd_pp_kernel<D, G, CAUSAL, DROP>), dim3(a.total), dim3(T::NT), 0, s, a);
 }
 
-// Dense and causal use the ping-pong kernel (256 query rows per workgroup,
-// one per CU) when it gets at least two workgroups per CU; smaller grids go
-// to the 128-row kernel (two workgroups per CU), which fills the chip with
-// twice as many workgroups (measured: +10-18% at B*H*N = 96K-100K, 8-18%
-// slower than the ping-pong kernel from 512 ping-pong workgroups up).  A
-// block mask needs 128-row workgroups (one mask row each).
+template <int D, int G>
+long pp_workgroups(int BH, int N) {
+  return (long)BH * ((N + fa::FwdPPTile<D, G>::BR - 1) / fa::FwdPPTile<D, G>::BR);
+}
+
+// Dense and causal use the phased kernel (one workgroup per CU) when it gets
+// at least two workgroups per CU; smaller grids go to the 128-row kernel
+// (two workgroups per CU), which fills the chip with more workgroups
+// (measured: +10-18% at B*H*N = 96K-100K, 8-18% slower than the two-group
+// kernel from 512 of its workgroups up).  The three-group kernel (384 rows,
+// d=64 without dropout, whose generator does not fit beside it in 168
+// registers per wave) runs from N = 4096 up: there its per-tile rounds are
+// ~18% shorter (+11% on a dense grid of 16 workgroups per CU), while at
+// short N its 384-row tiles leave ragged tails.  A block mask needs 128-row
+// workgroups (one mask row each).
 constexpr long kPingPongMinWorkgroups = 512;
+constexpr int kThreeGroupMinN = 4096;
 
 template <int D, bool DROP>
 void launch_fwd_dd(const fa::FwdArgs& a, int BH, bool causal, bool mask, hipStream_t s) {
-  const long pp_wgs = (long)BH * ((a.N + fa::FwdPPTile<D>::BR - 1) / fa::FwdPPTile<D>::BR);
   if (mask) {
     if (causal) launch_fwd_t<D, true, true, DROP>(a, a.total, s);
     else launch_fwd_t<D, false, true, DROP>(a, a.total, s);
-  } else if (pp_wgs < kPingPongMinWorkgroups) {
+    return;
+  }
+  if constexpr (D == 64 && !DROP) {
+    if (a.N >= kThreeGroupMinN && pp_workgroups<D, 3>(BH, a.N) >= kPingPongMinWorkgroups) {
+      if (causal) launch_fwd_pp<D, 3, true, DROP>(a, BH, s);
+      else launch_fwd_pp<D, 3, false, DROP>(a, BH, s);
+      return;
+    }
+  }
+  if (pp_workgroups<D, 2>(BH, a.N) < kPingPongMinWorkgroups) {
     if (causal) launch_fwd_t<D, true, false, DROP>(a, a.total, s);
     else launch_fwd_t<D, false, false, DROP>(a, a.total, s);
   } else {
-    if (causal) launch_fwd_pp<D, true, DROP>(a, BH, s);
-    else launch_fwd_pp<D, false, DROP>(a, BH, s);
+    if (causal) launch_fwd_pp<D, 2, true, DROP>(a, BH, s);
+    else launch_fwd_pp<D, 2, false, DROP>(a, BH, s);
   }
 }
 

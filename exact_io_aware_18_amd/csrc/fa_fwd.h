@@ -372,31 +372,46 @@ __global__ __launch_bounds__(256, FwdTile<D>::MIN_WG) void fwd_bf16_kernel(FwdAr
   }
 }
 
-// ---- ping-pong forward (dense and causal) -----------------------------------
-// One workgroup of eight waves owns 256 query rows: waves 0-3 (group A) the
-// first 128, waves 4-7 (group B) the next 128; waves w and w+4 share a SIMD.
-// Per key tile a wave does a matrix phase M (O^T += V^T P^T of the previous
-// tile, then S^T = K Q^T of this tile) and a vector phase V (softmax of this
-// tile's scores).  Barriers hold the two groups half a tile apart, so on every
-// SIMD one wave's products run while the other wave's softmax runs:
+// ---- phased forward (dense and causal) --------------------------------------
+// One workgroup of G groups of four waves owns 128 G query rows: group g
+// (waves 4g .. 4g+3) owns rows 128 g .. +127 of the tile, and wave w runs on
+// SIMD w % 4, so every SIMD holds one wave of each group.  Per key tile a
+// wave does a matrix phase M (O^T += V^T P^T of the previous tile, then
+// S^T = K Q^T of this tile) and a vector phase (softmax of this tile's
+// scores).  Barriers split a round (one key tile) into G phases and hold the
+// groups one phase apart, so in every phase one wave per SIMD issues products
+// while the others run softmax.
+//
+// G = 2 (ping-pong): the vector phase is one step V.
 //   round r, phase 1:  A: M(r)      B: V(r-1)
 //   round r, phase 2:  A: V(r)      B: M(r)
+// G = 3: a single wave issues VALU work at about half the rate a SIMD can
+// retire it (measured: two VALU-bound waves on one SIMD each run at the
+// speed of one alone), so the softmax is split into two steps V1 (scores of
+// the first 32 keys) and V2 (the other 32, the max check and the bf16
+// conversion), and two waves per SIMD run softmax while the third runs its
+// products:
+//   round r, phase 1:  A: M(r)      B: V2(r-1)   C: V1(r-1)
+//   round r, phase 2:  A: V1(r)     B: M(r)      C: V2(r-1)
+//   round r, phase 3:  A: V2(r)     B: V1(r)     C: M(r)
 // Round r reads K(r) and V(r-1); K(r+1) and V(r) are copied meanwhile into
-// the buffers round r-1 finished with.
-template <int D>
+// the buffers round r-1 finished with (by the first 512 threads).
+template <int D, int G = 2>
 struct FwdPPTile {
-  static constexpr int NW = 8;
+  static constexpr int NW = 4 * G;
   static constexpr int NT = 64 * NW;
-  static constexpr int BR = 256;   // query rows per workgroup
-  static constexpr int BC = 64;    // keys per tile
+  static constexpr int BR = 128 * G;  // query rows per workgroup
+  static constexpr int BC = 64;       // keys per tile
   static constexpr int PITCH = 2 * D;
   static constexpr int T_BYTES = BC * PITCH;
+  static constexpr int CPT = 512;     // threads that copy the K/V tiles
 };
 
-template <int D, bool CAUSAL, bool DROP>
-__global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
-  using T = FwdPPTile<D>;
-  constexpr int BC = T::BC, BR = T::BR, NT = T::NT, PITCH = T::PITCH;
+template <int D, int G, bool CAUSAL, bool DROP>
+__global__ __launch_bounds__(256 * G, 1) void fwd_pp_kernel(FwdArgs a) {
+  using T = FwdPPTile<D, G>;
+  static_assert(G == 2 || G == 3, "two or three wave groups");
+  constexpr int BC = T::BC, BR = T::BR, PITCH = T::PITCH;
   constexpr int NKC = D / 16, NCT = D / 32;
   __shared__ __attribute__((aligned(1024))) char kb0[T::T_BYTES];
   __shared__ __attribute__((aligned(1024))) char kb1[T::T_BYTES];
@@ -405,7 +420,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool grpA = w < 4;
+  const int grp = w >> 2;
   const int h = lane >> 5, li = lane & 31;
 
   const int g = xcd_remap(blockIdx.x, a.total);
@@ -431,8 +446,9 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   }
   TileOffsets<D> toff;
   toff.init(lane);
-  TileCopy<BC, D, NT> cp;
+  TileCopy<BC, D, T::CPT> cp;
   cp.init(w, lane);
+  const bool copier = w < T::CPT / 64;
 
   f32x16 o[NCT];
 #pragma unroll
@@ -486,8 +502,57 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
     }
   };
 
-  // vector phase: softmax of the scores of tile r into pb
-  auto vphase = [&] __device__ (int r) __attribute__((always_inline)) {
+  // vector phase: softmax of the scores of tile r into pb, in two steps.
+  // P = 2^(S*c - Mref) against the current reference.  The row max is
+  // needed only when a row has no reference yet or some P of this tile
+  // would exceed 2^kSkipLog2: then the reference moves (lazily, as in the
+  // other kernel) and P is recomputed.  Either way O / l and lse use the
+  // same reference, so the result does not depend on which path ran.
+  // Step 1 masks the tile and takes P of its first 32 keys; step 2 the rest,
+  // the check, the slow path if needed, and the bf16 P.  Run back to back,
+  // the steps are the single vector phase of the two-group schedule.
+  float p0[16], p1[16];
+  float lt0 = 0.f;
+  auto exps0 = [&] __device__ (float mb) __attribute__((always_inline)) -> float {
+    float ls[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p0[8 * hh + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[8 * hh + e], c, -mb));
+      const float* a0 = p0 + 8 * hh;
+      ls[hh] = ((a0[0] + a0[1]) + (a0[2] + a0[3])) + ((a0[4] + a0[5]) + (a0[6] + a0[7]));
+    }
+    return ls[0] + ls[1];
+  };
+  auto exps1 = [&] __device__ (float mb) __attribute__((always_inline)) -> float {
+    float ls[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p1[8 * hh + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[8 * hh + e], c, -mb));
+      const float* a1 = p1 + 8 * hh;
+      ls[hh] = ((a1[0] + a1[1]) + (a1[2] + a1[3])) + ((a1[4] + a1[5]) + (a1[6] + a1[7]));
+    }
+    return ls[0] + ls[1];
+  };
+  // bf16 P of the first / last 32 keys of the tile (after the dropout mask)
+  auto conv0 = [&] __device__ (int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      if constexpr (DROP) drop8(a.drop, bh, qi, k0 + 16 * hh + 8 * h, p0 + 8 * hh);
+      const float* a0 = p0 + 8 * hh;
+      pb[hh] = to_bf16x8(a0[0], a0[1], a0[2], a0[3], a0[4], a0[5], a0[6], a0[7]);
+    }
+  };
+  auto conv1 = [&] __device__ (int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      if constexpr (DROP) drop8(a.drop, bh, qi, k0 + 32 + 16 * hh + 8 * h, p1 + 8 * hh);
+      const float* a1 = p1 + 8 * hh;
+      pb[2 + hh] = to_bf16x8(a1[0], a1[1], a1[2], a1[3], a1[4], a1[5], a1[6], a1[7]);
+    }
+  };
+  auto vstep1 = [&] __device__ (int r) __attribute__((always_inline)) {
     if (r < 0 || r >= wtiles) return;
     const int k0 = r * BC;
     const bool edge = (CAUSAL && k0 + BC - 1 > qw0) || (k0 + BC > N);
@@ -499,32 +564,18 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
         if ((CAUSAL && key1 > qi) || key1 >= N) s1[e] = -INFINITY;
       }
     }
-    // P = 2^(S*c - Mref) against the current reference.  The row max is
-    // needed only when a row has no reference yet or some P of this tile
-    // would exceed 2^kSkipLog2: then the reference moves (lazily, as in the
-    // other kernel) and P is recomputed.  Either way O / l and lse use the
-    // same reference, so the result does not depend on which path ran.
-    float p0[16], p1[16];
-    auto exps = [&] __device__ (float mb) __attribute__((always_inline)) -> float {
-      float ls[4];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          p0[8 * hh + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[8 * hh + e], c, -mb));
-          p1[8 * hh + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[8 * hh + e], c, -mb));
-        }
-        const float* a0 = p0 + 8 * hh;
-        const float* a1 = p1 + 8 * hh;
-        ls[hh] = ((a0[0] + a0[1]) + (a0[2] + a0[3])) + ((a0[4] + a0[5]) + (a0[6] + a0[7]));
-        ls[2 + hh] = ((a1[0] + a1[1]) + (a1[2] + a1[3])) + ((a1[4] + a1[5]) + (a1[6] + a1[7]));
-      }
-      return (ls[0] + ls[1]) + (ls[2] + ls[3]);
-    };
+    if (Mref != -INFINITY) {
+      lt0 = exps0(Mref);
+      conv0(k0);
+    }
+  };
+  auto vstep2 = [&] __device__ (int r) __attribute__((always_inline)) {
+    if (r < 0 || r >= wtiles) return;
+    const int k0 = r * BC;
     bool slow = wave_any(Mref == -INFINITY);
     float lt = 0.f;
     if (!slow) {
-      lt = exps(Mref);
+      lt = lt0 + exps1(Mref);
       slow = wave_any(!(lt <= kSkipSum));  // also catches inf / NaN
     }
     if (slow) {
@@ -545,59 +596,89 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
         for (int ct = 0; ct < NCT; ++ct) o[ct] *= alpha;
         Mref = Mn;
       }
-      lt = exps((Mref == -INFINITY) ? 0.f : Mref);
+      const float mb = (Mref == -INFINITY) ? 0.f : Mref;
+      lt = exps0(mb);
+      conv0(k0);
+      lt = lt + exps1(mb);
     }
     L += lt;
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      if constexpr (DROP) {
-        drop8(a.drop, bh, qi, k0 + 16 * hh + 8 * h, p0 + 8 * hh);
-        drop8(a.drop, bh, qi, k0 + 32 + 16 * hh + 8 * h, p1 + 8 * hh);
-      }
-      const float* a0 = p0 + 8 * hh;
-      const float* a1 = p1 + 8 * hh;
-      pb[hh] = to_bf16x8(a0[0], a0[1], a0[2], a0[3], a0[4], a0[5], a0[6], a0[7]);
-      pb[2 + hh] = to_bf16x8(a1[0], a1[1], a1[2], a1[3], a1[4], a1[5], a1[6], a1[7]);
-    }
+    conv1(k0);
   };
 
   // prologue: K(0) into kb0
-  if (ntiles > 0) cp.issue(kb0, Kh, 0, N, w);
+  if (ntiles > 0 && copier) cp.issue(kb0, Kh, 0, N, w);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   // round r (r = 0 .. ntiles): K(r) in kb[r&1], V(r-1) in vb[(r-1)&1].
-  // Each group runs its own loop (the phase order differs); both execute the
-  // same two barriers per round.
+  // Each group runs its own loop (the phase order differs); all execute the
+  // same G barriers per round, the last after waiting for the copies.
   auto copies = [&] __device__ (int r, char* knext, char* vcur) __attribute__((always_inline)) {
+    if (!copier) return;
     if (r + 1 < ntiles) cp.issue(knext, Kh, (r + 1) * BC, N, w);
     if (r < ntiles) cp.issue(vcur, Vh, r * BC, N, w);
   };
-  if (grpA) {
-    auto roundA = [&] __device__ (int r, const char* kcur, char* knext, const char* vprev, char* vcur) __attribute__((always_inline)) {
-      copies(r, knext, vcur);
-      mphase(r, kcur, vprev);
-      __syncthreads();
-      vphase(r);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-    };
+  auto endround = [&] __device__ () __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+  auto rounds = [&] __device__ (auto&& round) __attribute__((always_inline)) {
     for (int r = 0; r <= ntiles; r += 2) {
-      roundA(r, kb0, kb1, vb1, vb0);
-      if (r + 1 <= ntiles) roundA(r + 1, kb1, kb0, vb0, vb1);
+      round(r, kb0, kb1, vb1, vb0);
+      if (r + 1 <= ntiles) round(r + 1, kb1, kb0, vb0, vb1);
+    }
+  };
+  if constexpr (G == 2) {
+    if (grp == 0) {
+      rounds([&] __device__ (int r, const char* kcur, char* knext, const char* vprev, char* vcur) __attribute__((always_inline)) {
+        copies(r, knext, vcur);
+        mphase(r, kcur, vprev);
+        __syncthreads();
+        vstep1(r);
+        vstep2(r);
+        endround();
+      });
+    } else {
+      rounds([&] __device__ (int r, const char* kcur, char* knext, const char* vprev, char* vcur) __attribute__((always_inline)) {
+        copies(r, knext, vcur);
+        vstep1(r - 1);
+        vstep2(r - 1);
+        __syncthreads();
+        mphase(r, kcur, vprev);
+        endround();
+      });
     }
   } else {
-    auto roundB = [&] __device__ (int r, const char* kcur, char* knext, const char* vprev, char* vcur) __attribute__((always_inline)) {
-      copies(r, knext, vcur);
-      vphase(r - 1);
-      __syncthreads();
-      mphase(r, kcur, vprev);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-    };
-    for (int r = 0; r <= ntiles; r += 2) {
-      roundB(r, kb0, kb1, vb1, vb0);
-      if (r + 1 <= ntiles) roundB(r + 1, kb1, kb0, vb0, vb1);
+    if (grp == 0) {
+      rounds([&] __device__ (int r, const char* kcur, char* knext, const char* vprev, char* vcur) __attribute__((always_inline)) {
+        copies(r, knext, vcur);
+        mphase(r, kcur, vprev);
+        __syncthreads();
+        vstep1(r);
+        __syncthreads();
+        vstep2(r);
+        endround();
+      });
+    } else if (grp == 1) {
+      rounds([&] __device__ (int r, const char* kcur, char* knext, const char* vprev, char* vcur) __attribute__((always_inline)) {
+        copies(r, knext, vcur);
+        vstep2(r - 1);
+        __syncthreads();
+        mphase(r, kcur, vprev);
+        __syncthreads();
+        vstep1(r);
+        endround();
+      });
+    } else {
+      rounds([&] __device__ (int r, const char* kcur, char* knext, const char* vprev, char* vcur) __attribute__((always_inline)) {
+        copies(r, knext, vcur);
+        vstep1(r - 1);
+        __syncthreads();
+        vstep2(r - 1);
+        __syncthreads();
+        mphase(r, kcur, vprev);
+        endround();
+      });
     }
   }
 

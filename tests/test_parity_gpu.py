@@ -229,3 +229,29 @@ def test_pingpong_grid_sizes(d, causal):
     full-parity tests) take the 128-row kernel."""
     q, k, v, do = make_qkvdo(2, 64, 1000, d, "bf16", seed=41)
     full_parity(q, k, v, do, default_scale(d), causal, None, "bf16")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_three_group_forward(causal):
+    """The 384-row three-group forward (d = 64, N >= 4096, at least 512 of its
+    workgroups): B*H = 48 and N = 4100, so the grid is 528 workgroups and the
+    last query tile of every head holds 260 rows.  O and lse at 256 seeded
+    rows plus the edge rows of two heads, against the oracle."""
+    dev = device()
+    B, H, N, d = 2, 24, 4100, 64
+    scale = default_scale(d)
+    q, k, v, do = make_qkvdo(B, H, N, d, "bf16", seed=51)
+    print(f"\n[three-group] shape={(B, H, N, d)} causal={causal}", flush=True)
+    got = run_gpu(q, k, v, do, scale, causal, None, "bf16", dev, backward=False)
+    b, h, i = (x.numpy() for x in sample_rows(B, H, N))
+    edge = np.array([0, 1, 31, 32, 383, 384, 767, 3839, 3840, 4095, 4096, N - 1])
+    ne = len(edge)
+    b = np.concatenate([b, np.zeros(ne, dtype=b.dtype), np.full(ne, B - 1, dtype=b.dtype)])
+    h = np.concatenate([h, np.zeros(ne, dtype=h.dtype), np.full(ne, H - 1, dtype=h.dtype)])
+    i = np.concatenate([i, edge.astype(i.dtype), edge.astype(i.dtype)])
+    q64, k64, v64 = (to64(t) for t in (q, k, v))
+    rep = {}
+    o_ref, lse_ref = attention_fwd_rows(q64, k64, v64, scale, causal, None, b, h, i)
+    check("o", to64(got["o"])[b, h, i], o_ref, "bf16", rep)
+    check("lse", to64(got["lse"])[b, h, i], lse_ref, "bf16", rep)
+    print("[three-group] max-abs:", {k_: f"{v_:.2e}" for k_, v_ in rep.items()}, flush=True)
