@@ -395,7 +395,12 @@ __global__ __launch_bounds__(256, FwdTile<D>::MIN_WG) void fwd_bf16_kernel(FwdAr
 //   round r, phase 2:  A: V1(r)     B: M(r)      C: V2(r-1)
 //   round r, phase 3:  A: V2(r)     B: V1(r)     C: M(r)
 // Round r reads K(r) and V(r-1); K(r+1) and V(r) are copied meanwhile into
-// the buffers round r-1 finished with (by the first 512 threads).
+// the buffers round r-1 finished with.  Only group 0 issues the copies,
+// inside its matrix phase (K before the PV products, V between the PV and
+// score products): direct-to-LDS copies queue for the CU's address unit,
+// and a wave stalls while its copies issue, so issuing them from every wave
+// at the start of a round lengthened that round's first phase by ~300
+// cycles for all groups.
 template <int D, int G = 2>
 struct FwdPPTile {
   static constexpr int NW = 4 * G;
@@ -404,7 +409,7 @@ struct FwdPPTile {
   static constexpr int BC = 64;       // keys per tile
   static constexpr int PITCH = 2 * D;
   static constexpr int T_BYTES = BC * PITCH;
-  static constexpr int CPT = 512;     // threads that copy the K/V tiles
+  static constexpr int CPT = 256;     // threads that copy the K/V tiles (group 0)
 };
 
 template <int D, int G, bool CAUSAL, bool DROP>
@@ -448,7 +453,7 @@ __global__ __launch_bounds__(256 * G, 1) void fwd_pp_kernel(FwdArgs a) {
   toff.init(lane);
   TileCopy<BC, D, T::CPT> cp;
   cp.init(w, lane);
-  const bool copier = w < T::CPT / 64;
+  const bool copier = grp == 0;
 
   f32x16 o[NCT];
 #pragma unroll
@@ -464,7 +469,7 @@ __global__ __launch_bounds__(256 * G, 1) void fwd_pp_kernel(FwdArgs a) {
   bf16x8 pb[4];   // P of the previous tile (bf16)
 
   // matrix phase of round r: O^T += V^T P^T for tile r-1, then S^T of tile r
-  auto mphase = [&] __device__ (int r, const char* kt, const char* vprev) __attribute__((always_inline)) {
+  auto mphase = [&] __device__ (int r, const char* kt, const char* vprev, auto&& mid) __attribute__((always_inline)) {
     if (r >= 1 && r - 1 < wtiles) {
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
@@ -478,6 +483,7 @@ __global__ __launch_bounds__(256 * G, 1) void fwd_pp_kernel(FwdArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    mid();
     if (r < wtiles) {
       bf16x8 ka0[NKC], ka1[NKC];
 #pragma unroll
@@ -613,11 +619,15 @@ __global__ __launch_bounds__(256 * G, 1) void fwd_pp_kernel(FwdArgs a) {
   // round r (r = 0 .. ntiles): K(r) in kb[r&1], V(r-1) in vb[(r-1)&1].
   // Each group runs its own loop (the phase order differs); all execute the
   // same G barriers per round, the last after waiting for the copies.
-  auto copies = [&] __device__ (int r, char* knext, char* vcur) __attribute__((always_inline)) {
-    if (!copier) return;
-    if (r + 1 < ntiles) cp.issue(knext, Kh, (r + 1) * BC, N, w);
-    if (r < ntiles) cp.issue(vcur, Vh, r * BC, N, w);
+  // mphase runs its last argument between the PV and the score products.
+  // copies issued by group 0 (see the schedule above)
+  auto copyk = [&] __device__ (int r, char* knext) __attribute__((always_inline)) {
+    if (copier && r + 1 < ntiles) cp.issue(knext, Kh, (r + 1) * BC, N, w);
   };
+  auto copyv = [&] __device__ (int r, char* vcur) __attribute__((always_inline)) {
+    if (copier && r < ntiles) cp.issue(vcur, Vh, r * BC, N, w);
+  };
+  auto nomid = [] __device__ () {};
   auto endround = [&] __device__ () __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -631,8 +641,8 @@ __global__ __launch_bounds__(256 * G, 1) void fwd_pp_kernel(FwdArgs a) {
   if constexpr (G == 2) {
     if (grp == 0) {
       rounds([&] __device__ (int r, const char* kcur, char* knext, const char* vprev, char* vcur) __attribute__((always_inline)) {
-        copies(r, knext, vcur);
-        mphase(r, kcur, vprev);
+        copyk(r, knext);
+        mphase(r, kcur, vprev, [&] __device__ () { copyv(r, vcur); });
         __syncthreads();
         vstep1(r);
         vstep2(r);
@@ -640,19 +650,18 @@ __global__ __launch_bounds__(256 * G, 1) void fwd_pp_kernel(FwdArgs a) {
       });
     } else {
       rounds([&] __device__ (int r, const char* kcur, char* knext, const char* vprev, char* vcur) __attribute__((always_inline)) {
-        copies(r, knext, vcur);
         vstep1(r - 1);
         vstep2(r - 1);
         __syncthreads();
-        mphase(r, kcur, vprev);
+        mphase(r, kcur, vprev, nomid);
         endround();
       });
     }
   } else {
     if (grp == 0) {
       rounds([&] __device__ (int r, const char* kcur, char* knext, const char* vprev, char* vcur) __attribute__((always_inline)) {
-        copies(r, knext, vcur);
-        mphase(r, kcur, vprev);
+        copyk(r, knext);
+        mphase(r, kcur, vprev, [&] __device__ () { copyv(r, vcur); });
         __syncthreads();
         vstep1(r);
         __syncthreads();
@@ -661,22 +670,20 @@ __global__ __launch_bounds__(256 * G, 1) void fwd_pp_kernel(FwdArgs a) {
       });
     } else if (grp == 1) {
       rounds([&] __device__ (int r, const char* kcur, char* knext, const char* vprev, char* vcur) __attribute__((always_inline)) {
-        copies(r, knext, vcur);
         vstep2(r - 1);
         __syncthreads();
-        mphase(r, kcur, vprev);
+        mphase(r, kcur, vprev, nomid);
         __syncthreads();
         vstep1(r);
         endround();
       });
     } else {
       rounds([&] __device__ (int r, const char* kcur, char* knext, const char* vprev, char* vcur) __attribute__((always_inline)) {
-        copies(r, knext, vcur);
         vstep1(r - 1);
         __syncthreads();
         vstep2(r - 1);
         __syncthreads();
-        mphase(r, kcur, vprev);
+        mphase(r, kcur, vprev, nomid);
         endround();
       });
     }
