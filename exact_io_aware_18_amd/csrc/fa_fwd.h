@@ -387,10 +387,10 @@ __global__ __launch_bounds__(256, FwdTile<D>::MIN_WG) void fwd_bf16_kernel(FwdAr
 //   round r, phase 2:  A: V(r)      B: M(r)
 // G = 3: a single wave issues VALU work at about half the rate a SIMD can
 // retire it (measured: two VALU-bound waves on one SIMD each run at the
-// speed of one alone), so the softmax is split into two steps V1 (scores of
-// the first 32 keys) and V2 (the other 32, the max check and the bf16
-// conversion), and two waves per SIMD run softmax while the third runs its
-// products:
+// speed of one alone), so the softmax is split into two steps V1 (mask, P and
+// bf16 P of the tile's first 32 keys) and V2 (the other 32 keys, the max
+// check and the slow path when it is needed), and two waves per SIMD run
+// softmax while the third runs its products:
 //   round r, phase 1:  A: M(r)      B: V2(r-1)   C: V1(r-1)
 //   round r, phase 2:  A: V1(r)     B: M(r)      C: V2(r-1)
 //   round r, phase 3:  A: V2(r)     B: V1(r)     C: M(r)
@@ -514,9 +514,11 @@ __global__ __launch_bounds__(256 * G, 1) void fwd_pp_kernel(FwdArgs a) {
   // would exceed 2^kSkipLog2: then the reference moves (lazily, as in the
   // other kernel) and P is recomputed.  Either way O / l and lse use the
   // same reference, so the result does not depend on which path ran.
-  // Step 1 masks the tile and takes P of its first 32 keys; step 2 the rest,
-  // the check, the slow path if needed, and the bf16 P.  Run back to back,
-  // the steps are the single vector phase of the two-group schedule.
+  // Step 1 masks the tile and takes P (and its bf16 copy) of the first 32
+  // keys; step 2 the other 32, the check, and the slow path if needed, which
+  // recomputes both halves.  Run back to back, the steps are the single
+  // vector phase of the two-group schedule; each element is computed the
+  // same way in both, so the two schedules give bitwise identical results.
   float p0[16], p1[16];
   float lt0 = 0.f;
   auto exps0 = [&] __device__ (float mb) __attribute__((always_inline)) -> float {
