@@ -231,17 +231,21 @@ def test_pingpong_grid_sizes(d, causal):
     full_parity(q, k, v, do, default_scale(d), causal, None, "bf16")
 
 
-@pytest.mark.parametrize("causal", [False, True])
-def test_three_group_forward(causal):
+@pytest.mark.parametrize("causal,sign", [(False, 1.0), (True, 1.0), (True, -1.0)])
+def test_three_group_forward(causal, sign):
     """The 384-row three-group forward (d = 64, N >= 4096, at least 512 of its
     workgroups): B*H = 48 and N = 4100, so the grid is 528 workgroups and the
     last query tile of every head holds 260 rows.  O and lse at 256 seeded
-    rows plus the edge rows of two heads, against the oracle."""
+    rows plus the edge rows of two heads, against the oracle; a negative
+    scale (scores computed with -Q and |scale|); and a second call that must
+    repeat the first bit for bit."""
+    import exact_io_aware_18_amd as fa
+
     dev = device()
     B, H, N, d = 2, 24, 4100, 64
-    scale = default_scale(d)
+    scale = sign * default_scale(d)
     q, k, v, do = make_qkvdo(B, H, N, d, "bf16", seed=51)
-    print(f"\n[three-group] shape={(B, H, N, d)} causal={causal}", flush=True)
+    print(f"\n[three-group] shape={(B, H, N, d)} causal={causal} scale={scale}", flush=True)
     got = run_gpu(q, k, v, do, scale, causal, None, "bf16", dev, backward=False)
     b, h, i = (x.numpy() for x in sample_rows(B, H, N))
     edge = np.array([0, 1, 31, 32, 383, 384, 767, 3839, 3840, 4095, 4096, N - 1])
@@ -255,3 +259,14 @@ def test_three_group_forward(causal):
     check("o", to64(got["o"])[b, h, i], o_ref, "bf16", rep)
     check("lse", to64(got["lse"])[b, h, i], lse_ref, "bf16", rep)
     print("[three-group] max-abs:", {k_: f"{v_:.2e}" for k_, v_ in rep.items()}, flush=True)
+    o2, l2 = fa.fwd(q.to(dev), k.to(dev), v.to(dev), scale, causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o2.cpu(), got["o"]) and torch.equal(l2.cpu(), got["lse"])
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_pingpong_negative_scale(d):
+    """The two-group kernel (B*H = 128, N = 1000: 512 workgroups) with a
+    negative scale, forward and backward against the oracle."""
+    q, k, v, do = make_qkvdo(2, 64, 1000, d, "bf16", seed=43)
+    full_parity(q, k, v, do, -default_scale(d), True, None, "bf16")
