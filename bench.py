@@ -220,9 +220,12 @@ def sweep(kind, reps):
     sparsity: B=1, H=16, N=16384, d=64, block masks keeping the diagonal plus a
       fraction f of the off-diagonal 128x128 blocks; forward and backward time
       against the number of unmasked pairs (runtime should follow density).
-    io: B=1, H=16, non-causal, d=64 and 128, N in IO_SEQS, forward only, with
-      two query-tile heights: Br=256 (the ping-pong kernel, no mask) and
-      Br=128 (the block-mask kernel with an all-ones mask, the same result).
+    io: non-causal, d=64 and 128, N in IO_SEQS with B*H = 16 * 16384 / N heads
+      (the same number of query rows at every N, so every point fills the
+      chip), forward only, twice per point: without a mask (the kernel the
+      dispatch picks; its query-tile height Br, 256 or 384, from
+      fa_fwd_query_rows) and with an all-ones block mask (Br = 128, the same
+      result).
       Run under rocprofv3 --pmc to read the bytes each launch moves; the
       launches come in the printed order, `reps` + 1 per point.
     """
@@ -253,24 +256,27 @@ def sweep(kind, reps):
                               "fwd_tflops": round(4.0 * d * pairs / tf / 1e9, 1),
                               "bwd_tflops": round(10.0 * d * pairs / tb / 1e9, 1)}), flush=True)
     elif kind == "io":
-        B, H = 1, 16
         for d in (64, 128):
             for N in IO_SEQS:
+                B, H = 1, 16 * 16384 // N
                 q, k, v, _ = (t.to(dev) for t in make_qkvdo(B, H, N, d, "bf16", seed=0))
                 o = torch.empty_like(q)
                 lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
                 nb = (N + 127) // 128
                 ones = torch.ones((nb, nb), dtype=torch.uint8, device=dev)
-                for br, m in ((256, None), (128, ones)):
+                for m in (None, ones):
+                    br = fa.fa_fwd_query_rows(B, H, N, d, 0, m is not None, 0)
                     t = _time_calls(lambda: fa.fwd(q, k, v, default_scale(d), False, m, out=o, lse=lse), reps)
                     # bytes of the tiled algorithm without cache reuse: K and V
                     # read once per query tile, Q read and O, lse written once
-                    model = B * H * ((N // br) * 2 * N * d * 2 + 2 * N * d * 2 + N * 4)
+                    ntq = (N + br - 1) // br
+                    model = B * H * (ntq * 2 * N * d * 2 + 2 * N * d * 2 + N * 4)
                     print(json.dumps({"sweep": "io", "B": B, "H": H, "N": N, "d": d, "Br": br,
-                                      "fwd_ms": round(t, 4),
+                                      "mask": m is not None, "fwd_ms": round(t, 4),
                                       "tflops": round(4.0 * d * B * H * N * N / t / 1e9, 1),
                                       "io_model_bytes": model,
                                       "compulsory_bytes": B * H * (4 * N * d * 2 + N * 4)}), flush=True)
+                del q, k, v, o, lse
     elif kind == "decode":
         # few queries against a long cache: K and V are streamed once, so the
         # bound is HBM bandwidth (bytes = K + V + Q + O + lse per call)

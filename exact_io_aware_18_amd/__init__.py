@@ -8,7 +8,7 @@ raises; there is no fallback implementation.
 Low level: one function per exported symbol (fa_fwd, fa_bwd, the three
 backward stages, fa_fwd_dropout, fa_bwd_dropout, fa_fwd_decode,
 fa_decode_workspace_bytes, fa_fwd_f32, fa_bwd_f32, fa_bwd_workspace_bytes,
-fa_strerror, fa_version) takes the C arguments as they are (pointers as
+fa_fwd_query_rows, fa_strerror, fa_version) takes the C arguments as they are (pointers as
 integers).  High level: fwd, bwd, bwd_stages, fwd_dropout, bwd_dropout,
 decode, fwd_f32 and bwd_f32 take torch tensors, allocate the outputs and
 raise FAError on a nonzero status.
@@ -29,7 +29,7 @@ STATUS_NAMES = {
 }
 EXPORTED = ("fa_fwd", "fa_bwd", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq",
             "fa_fwd_dropout", "fa_bwd_dropout", "fa_fwd_decode", "fa_decode_workspace_bytes",
-            "fa_bwd_workspace_bytes", "fa_fwd_f32",
+            "fa_bwd_workspace_bytes", "fa_fwd_query_rows", "fa_fwd_f32",
             "fa_bwd_f32", "fa_strerror", "fa_version")
 
 _lib = None
@@ -73,6 +73,8 @@ def lib() -> ctypes.CDLL:
         L.fa_bwd_f32.argtypes = L.fa_bwd.argtypes
         L.fa_bwd_f32.restype = I
         L.fa_bwd_workspace_bytes.argtypes = [I, I, I, I]
+        L.fa_fwd_query_rows.argtypes = [I, I, I, I, I, I, I]
+        L.fa_fwd_query_rows.restype = I
         L.fa_bwd_workspace_bytes.restype = Z
         L.fa_strerror.argtypes = [I]
         L.fa_strerror.restype = ctypes.c_char_p
@@ -143,6 +145,10 @@ def fa_bwd_f32(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, blo
 
 def fa_bwd_workspace_bytes(B, H, N, d) -> int:
     return lib().fa_bwd_workspace_bytes(B, H, N, d)
+
+
+def fa_fwd_query_rows(B, H, N, d, causal, has_blockmask, dropout) -> int:
+    return lib().fa_fwd_query_rows(B, H, N, d, int(causal), int(has_blockmask), int(dropout))
 
 
 def fa_strerror(status: int) -> str:

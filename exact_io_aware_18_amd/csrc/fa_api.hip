@@ -101,27 +101,40 @@ long pp_workgroups(int BH, int N) {
 constexpr long kPingPongMinWorkgroups = 512;
 constexpr int kThreeGroupMinN = 4096;
 
+// Query rows per workgroup of the bf16 forward kernel a call takes: 128
+// (block mask, or a small grid), 256 (two groups) or 384 (three groups).
+// The launch below and fa_fwd_query_rows both decide through this function.
+int fwd_rows(int BH, int N, int d, bool mask, bool drop) {
+  if (mask) return 128;
+  const bool g3 = d == 64 && !drop && N >= kThreeGroupMinN &&
+                  pp_workgroups<64, 3>(BH, N) >= kPingPongMinWorkgroups;
+  if (g3) return fa::FwdPPTile<64, 3>::BR;
+  const long g2 = d == 64 ? pp_workgroups<64, 2>(BH, N) : pp_workgroups<128, 2>(BH, N);
+  return g2 >= kPingPongMinWorkgroups ? fa::FwdPPTile<64, 2>::BR : fa::FwdTile<64>::BR;
+}
+
 template <int D, bool DROP>
 void launch_fwd_dd(const fa::FwdArgs& a, int BH, bool causal, bool mask, hipStream_t s) {
-  if (mask) {
-    if (causal) launch_fwd_t<D, true, true, DROP>(a, a.total, s);
-    else launch_fwd_t<D, false, true, DROP>(a, a.total, s);
+  const int rows = fwd_rows(BH, a.N, D, mask, DROP);
+  if (rows == 128) {
+    if (mask) {
+      if (causal) launch_fwd_t<D, true, true, DROP>(a, a.total, s);
+      else launch_fwd_t<D, false, true, DROP>(a, a.total, s);
+    } else {
+      if (causal) launch_fwd_t<D, true, false, DROP>(a, a.total, s);
+      else launch_fwd_t<D, false, false, DROP>(a, a.total, s);
+    }
     return;
   }
   if constexpr (D == 64 && !DROP) {
-    if (a.N >= kThreeGroupMinN && pp_workgroups<D, 3>(BH, a.N) >= kPingPongMinWorkgroups) {
+    if (rows == fa::FwdPPTile<D, 3>::BR) {
       if (causal) launch_fwd_pp<D, 3, true, DROP>(a, BH, s);
       else launch_fwd_pp<D, 3, false, DROP>(a, BH, s);
       return;
     }
   }
-  if (pp_workgroups<D, 2>(BH, a.N) < kPingPongMinWorkgroups) {
-    if (causal) launch_fwd_t<D, true, false, DROP>(a, a.total, s);
-    else launch_fwd_t<D, false, false, DROP>(a, a.total, s);
-  } else {
-    if (causal) launch_fwd_pp<D, 2, true, DROP>(a, BH, s);
-    else launch_fwd_pp<D, 2, false, DROP>(a, BH, s);
-  }
+  if (causal) launch_fwd_pp<D, 2, true, DROP>(a, BH, s);
+  else launch_fwd_pp<D, 2, false, DROP>(a, BH, s);
 }
 
 template <int D>
@@ -517,6 +530,14 @@ size_t fa_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d) {
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
   if (check_shape(B, H, N, d) != FA_OK) return 0;
   return workspace_bytes(B, H, N);
+}
+
+int fa_fwd_query_rows(int B, int H, int N, int d, int causal, int has_blockmask, int dropout) {
+  if (check_shape(B, H, N, d) != FA_OK) return 0;
+  if ((causal != 0 && causal != 1) || (has_blockmask != 0 && has_blockmask != 1) ||
+      (dropout != 0 && dropout != 1))
+    return 0;
+  return fwd_rows(B * H, N, d, has_blockmask != 0, dropout != 0);
 }
 
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,

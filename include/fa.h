@@ -161,6 +161,15 @@ size_t fa_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d);
 /* Bytes of workspace fa_bwd and fa_bwd_f32 need (0 for invalid sizes). */
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
 
+/* Query rows per workgroup (the outer tile height Br) of the kernel that
+ * fa_fwd (dropout = 0) or fa_fwd_dropout with p_drop > 0 (dropout = 1)
+ * launches for these sizes: 128, 256 or 384.  The tiled algorithm reads K
+ * and V once per query tile of Br rows ("Tiling", FlashAttention summary
+ * page, §3 Method), so this fixes the no-reuse IO term of a call.  Host
+ * only: no HIP call, no state.  Returns 0 for sizes or flags fa_fwd rejects
+ * (flags must be 0 or 1). */
+int fa_fwd_query_rows(int B, int H, int N, int d, int causal, int has_blockmask, int dropout);
+
 /* Forward with fp32 tensors throughout (fp32 arithmetic, fp32 O and lse). */
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o,
                float* lse, int B, int H, int N, int d, float scale,

@@ -62,6 +62,29 @@ def test_workspace_bytes(lib):
     assert fa.fa_bwd_workspace_bytes(1, 1, 10, 96) == 0
 
 
+def test_fwd_query_rows(lib):
+    q = fa.fa_fwd_query_rows
+    # block mask: one 128-row workgroup per mask row
+    assert q(1, 16, 65536, 64, 0, 1, 0) == 128
+    # small grids: the 128-row kernel (fewer than 512 two-group workgroups)
+    assert q(8, 12, 1024, 64, 1, 0, 0) == 128
+    assert q(1, 16, 4096, 128, 0, 0, 0) == 128
+    # exactly 512 two-group workgroups
+    assert q(2, 64, 1000, 64, 1, 0, 0) == 256
+    assert q(2, 64, 1000, 128, 0, 0, 0) == 256
+    # three groups at d = 64 from N = 4096 with at least 512 of their workgroups
+    assert q(1, 16, 16384, 64, 1, 0, 0) == 384
+    assert q(2, 24, 4100, 64, 0, 0, 0) == 384
+    assert q(2, 24, 4095, 64, 0, 0, 0) == 256     # N below 4096: two groups (768 workgroups)
+    assert q(1, 16, 16384, 64, 1, 0, 1) == 256   # dropout: two groups
+    assert q(1, 16, 16384, 128, 1, 0, 0) == 256  # d = 128: two groups
+    # rejected sizes and flags
+    assert q(0, 16, 4096, 64, 0, 0, 0) == 0
+    assert q(1, 16, 4096, 96, 0, 0, 0) == 0
+    assert q(1, 16, 4096, 64, 2, 0, 0) == 0
+    assert q(1, 16, 4096, 64, 0, 0, 3) == 0
+
+
 def fwd_args(B=1, H=2, N=256, d=64, esz=2, **over):
     tb = B * H * N * d * esz
     a = dict(q=BASE, k=BASE + 1 * tb + MB, v=BASE + 2 * (tb + MB), o=BASE + 3 * (tb + MB),
