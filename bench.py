@@ -560,6 +560,16 @@ def main():
                 "frac": round(achieved / peak, 4), "traffic": load_traffic(dom), "kernel": dom,
                 "kernel_ms": round(dk_["ms"], 4)}
 
+    # the same object for each forward kernel (the forward alone has its own
+    # target: a fraction of the bf16 MFMA peak at N >= 4K)
+    roofline_fwd = {}
+    for key, kv in kernels.items():
+        if key.startswith(kinds[0] + "_d") and "tflops" in kv:
+            roofline_fwd[key] = {"bound": "mfma", "achieved": round(kv["tflops"], 2), "peak": PEAK_BF16_TFLOPS,
+                                 "unit": "TFLOP/s", "frac": round(kv["tflops"] / PEAK_BF16_TFLOPS, 4),
+                                 "traffic": load_traffic(key) if drop == 0 else None,
+                                 "kernel_ms": round(kv["ms"], 4)}
+
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -586,6 +596,7 @@ def main():
         "kernels": {k_: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v_.items()}
                     for k_, v_ in kernels.items()},
         "roofline": roofline,
+        "roofline_fwd": roofline_fwd,
         "timing": "warm: back-to-back steps, per-kernel mean (ms) and p10/p50/p90 over the timed "
                   "steps from HIP events on the launch stream; cold: median over cold_steps steps, "
                   "each after writing %d MiB of scratch" % (COLD_FLUSH_BYTES >> 20),
