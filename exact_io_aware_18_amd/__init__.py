@@ -160,6 +160,10 @@ def fa_version() -> int:
 
 
 # ---- tensor-level wrappers ---------------------------------------------------
+# The C ABI reads raw pointers as contiguous [B, H, N, d] tensors of a fixed
+# dtype, so the wrappers check every tensor before a call: rank and shape
+# agreement, dtype, contiguity, then device.  Device placement is checked last
+# so that every other rejection can be exercised with CPU tensors.
 def _ptr(t):
     return None if t is None else t.data_ptr()
 
@@ -182,15 +186,116 @@ def _shape(q):
     return tuple(int(x) for x in q.shape)
 
 
-def fwd(q, k, v, scale, causal=False, blockmask=None, out=None, lse=None, stream=None):
-    """bf16 forward: returns (O bf16 [B,H,N,d], lse fp32 [B,H,N])."""
+class _Args:
+    """Collects the tensors of one call and validates them together."""
+
+    def __init__(self, where: str):
+        self.where = where
+        self.tensors = []  # (name, tensor)
+
+    def tensor(self, name, t, shape, dtypes):
+        import torch
+
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{self.where}: {name} must be a torch.Tensor")
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{self.where}: {name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if t.dtype not in dtypes:
+            names = " or ".join(str(d).replace("torch.", "") for d in dtypes)
+            raise ValueError(f"{self.where}: {name} has dtype {str(t.dtype).replace('torch.', '')}, "
+                             f"expected {names}")
+        if not t.is_contiguous():
+            raise ValueError(f"{self.where}: {name} must be contiguous ([B, H, N, d] row-major)")
+        self.tensors.append((name, t))
+        return t
+
+    def devices(self):
+        """Every tensor on one GPU; returns that device."""
+        dev = None
+        for name, t in self.tensors:
+            if not t.is_cuda:
+                raise ValueError(f"{self.where}: {name} must be on a GPU device, got {t.device}")
+            if dev is None:
+                dev = t.device
+            elif t.device != dev:
+                raise ValueError(f"{self.where}: {name} is on {t.device}, the other tensors on {dev}")
+        return dev
+
+
+def _dt(kind):
     import torch
 
-    B, H, N, d = _shape(q)
+    return {"bf16": (torch.bfloat16,), "f32": (torch.float32,),
+            "mask": (torch.uint8, torch.bool)}[kind]
+
+
+def _mask_shape(N):
+    nb = (N + 127) // 128
+    return (nb, nb)
+
+
+def _fwd_args(where, q, k, v, blockmask, out, lse, kind):
+    """Validate a forward call; allocate out / lse when not given."""
+    import torch
+
+    a = _Args(where)
+    shp = _shape(q)
+    B, H, N, d = shp
+    a.tensor("q", q, shp, _dt(kind))
+    a.tensor("k", k, shp, _dt(kind))
+    a.tensor("v", v, shp, _dt(kind))
+    if blockmask is not None:
+        a.tensor("blockmask", blockmask, _mask_shape(N), _dt("mask"))
+    if out is not None:
+        a.tensor("out", out, shp, _dt(kind))
+    if lse is not None:
+        a.tensor("lse", lse, (B, H, N), _dt("f32"))
+    dev = a.devices()
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty(shp, dtype=q.dtype, device=dev)
     if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    return shp, out, lse
+
+
+def _bwd_args(where, q, k, v, o, lse, dout, blockmask, grads, workspace, kind, ws_bytes):
+    """Validate a backward call; allocate the gradients and the workspace
+    when not given."""
+    import torch
+
+    a = _Args(where)
+    shp = _shape(q)
+    B, H, N, d = shp
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        a.tensor(name, t, shp, _dt(kind))
+    a.tensor("lse", lse, (B, H, N), _dt("f32"))
+    if blockmask is not None:
+        a.tensor("blockmask", blockmask, _mask_shape(N), _dt("mask"))
+    if grads is not None:
+        if len(grads) != 3:
+            raise ValueError(f"{where}: grads must be (dq, dk, dv)")
+        for name, t in zip(("dq", "dk", "dv"), grads):
+            a.tensor(name, t, shp, _dt("f32"))
+    if workspace is not None:
+        a.tensor("workspace", workspace, tuple(workspace.shape), (workspace.dtype,))
+        if workspace.numel() * workspace.element_size() < ws_bytes:
+            raise ValueError(f"{where}: workspace holds {workspace.numel() * workspace.element_size()} "
+                             f"bytes, {ws_bytes} needed")
+    dev = a.devices()
+    if grads is None:
+        grads = tuple(torch.empty(shp, dtype=torch.float32, device=dev) for _ in range(3))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    return shp, grads, workspace
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def fwd(q, k, v, scale, causal=False, blockmask=None, out=None, lse=None, stream=None):
+    """bf16 forward: returns (O bf16 [B,H,N,d], lse fp32 [B,H,N])."""
+    (B, H, N, d), out, lse = _fwd_args("fwd", q, k, v, blockmask, out, lse, "bf16")
     _check(fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, float(scale),
                   int(causal), _ptr(blockmask), _stream(stream)), "fa_fwd")
     return out, lse
@@ -199,35 +304,24 @@ def fwd(q, k, v, scale, causal=False, blockmask=None, out=None, lse=None, stream
 def bwd(q, k, v, o, lse, dout, scale, causal=False, blockmask=None, grads=None,
         workspace=None, stream=None):
     """bf16 backward: returns (dQ, dK, dV), fp32 [B,H,N,d]."""
-    import torch
-
     B, H, N, d = _shape(q)
-    if grads is None:
-        grads = tuple(torch.empty(q.shape, dtype=torch.float32, device=q.device) for _ in range(3))
-    dq, dk, dv = grads
-    wsb = fa_bwd_workspace_bytes(B, H, N, d)
-    if workspace is None:
-        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=q.device)
+    (B, H, N, d), (dq, dk, dv), workspace = _bwd_args(
+        "bwd", q, k, v, o, lse, dout, blockmask, grads, workspace, "bf16",
+        fa_bwd_workspace_bytes(B, H, N, d))
     _check(fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
                   _ptr(dv), B, H, N, d, float(scale), int(causal), _ptr(blockmask),
-                  _ptr(workspace), workspace.numel() * workspace.element_size(),
-                  _stream(stream)), "fa_bwd")
+                  _ptr(workspace), _nbytes(workspace), _stream(stream)), "fa_bwd")
     return dq, dk, dv
 
 
 def bwd_stages(q, k, v, o, lse, dout, scale, causal=False, blockmask=None, grads=None,
                workspace=None, stream=None):
     """The same backward as bwd() through its three stage calls, in order."""
-    import torch
-
     B, H, N, d = _shape(q)
-    if grads is None:
-        grads = tuple(torch.empty(q.shape, dtype=torch.float32, device=q.device) for _ in range(3))
-    dq, dk, dv = grads
-    wsb = fa_bwd_workspace_bytes(B, H, N, d)
-    if workspace is None:
-        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=q.device)
-    wn = workspace.numel() * workspace.element_size()
+    (B, H, N, d), (dq, dk, dv), workspace = _bwd_args(
+        "bwd_stages", q, k, v, o, lse, dout, blockmask, grads, workspace, "bf16",
+        fa_bwd_workspace_bytes(B, H, N, d))
+    wn = _nbytes(workspace)
     s = _stream(stream)
     _check(fa_bwd_preprocess(_ptr(o), _ptr(dout), B, H, N, d, _ptr(workspace), wn, s),
            "fa_bwd_preprocess")
@@ -243,13 +337,7 @@ def bwd_stages(q, k, v, o, lse, dout, scale, causal=False, blockmask=None, grads
 def fwd_dropout(q, k, v, scale, p_drop, seed, causal=False, blockmask=None, out=None, lse=None,
                 stream=None):
     """bf16 forward with dropout on P: returns (O bf16, lse fp32)."""
-    import torch
-
-    B, H, N, d = _shape(q)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    (B, H, N, d), out, lse = _fwd_args("fwd_dropout", q, k, v, blockmask, out, lse, "bf16")
     _check(fa_fwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, float(scale),
                           int(causal), _ptr(blockmask), float(p_drop), int(seed), _stream(stream)),
            "fa_fwd_dropout")
@@ -259,19 +347,14 @@ def fwd_dropout(q, k, v, scale, p_drop, seed, causal=False, blockmask=None, out=
 def bwd_dropout(q, k, v, o, lse, dout, scale, p_drop, seed, causal=False, blockmask=None,
                 grads=None, workspace=None, stream=None):
     """bf16 backward of fwd_dropout (same p_drop and seed): returns (dQ, dK, dV), fp32."""
-    import torch
-
     B, H, N, d = _shape(q)
-    if grads is None:
-        grads = tuple(torch.empty(q.shape, dtype=torch.float32, device=q.device) for _ in range(3))
-    dq, dk, dv = grads
-    wsb = fa_bwd_workspace_bytes(B, H, N, d)
-    if workspace is None:
-        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=q.device)
+    (B, H, N, d), (dq, dk, dv), workspace = _bwd_args(
+        "bwd_dropout", q, k, v, o, lse, dout, blockmask, grads, workspace, "bf16",
+        fa_bwd_workspace_bytes(B, H, N, d))
     _check(fa_bwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
                           _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(causal),
                           _ptr(blockmask), float(p_drop), int(seed), _ptr(workspace),
-                          workspace.numel() * workspace.element_size(), _stream(stream)),
+                          _nbytes(workspace), _stream(stream)),
            "fa_bwd_dropout")
     return dq, dk, dv
 
@@ -281,30 +364,40 @@ def decode(q, k, v, scale, causal=False, out=None, lse=None, workspace=None, str
     import torch
 
     B, H, Nq, d = _shape(q)
-    Nk = int(k.shape[2])
+    kshape = _shape(k)
+    a = _Args("decode")
+    a.tensor("q", q, (B, H, Nq, d), _dt("bf16"))
+    if kshape[0] != B or kshape[1] != H or kshape[3] != d:
+        raise ValueError(f"decode: k has shape {kshape}, expected ({B}, {H}, Nk, {d})")
+    Nk = kshape[2]
+    a.tensor("k", k, kshape, _dt("bf16"))
+    a.tensor("v", v, kshape, _dt("bf16"))
+    if out is not None:
+        a.tensor("out", out, (B, H, Nq, d), _dt("bf16"))
+    if lse is not None:
+        a.tensor("lse", lse, (B, H, Nq), _dt("f32"))
+    wsb = fa_decode_workspace_bytes(B, H, Nq, Nk, d)
+    if workspace is not None:
+        a.tensor("workspace", workspace, tuple(workspace.shape), (workspace.dtype,))
+        if _nbytes(workspace) < wsb:
+            raise ValueError(f"decode: workspace holds {_nbytes(workspace)} bytes, {wsb} needed")
+    dev = a.devices()
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty((B, H, Nq, d), dtype=torch.bfloat16, device=dev)
     if lse is None:
-        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
     if workspace is None:
-        workspace = torch.empty(max(fa_decode_workspace_bytes(B, H, Nq, Nk, d), 1), dtype=torch.uint8,
-                                device=q.device)
+        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
     _check(fa_fwd_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, d,
-                         float(scale), int(causal), _ptr(workspace),
-                         workspace.numel() * workspace.element_size(), _stream(stream)),
+                         float(scale), int(causal), _ptr(workspace), _nbytes(workspace),
+                         _stream(stream)),
            "fa_fwd_decode")
     return out, lse
 
 
 def fwd_f32(q, k, v, scale, causal=False, blockmask=None, out=None, lse=None, stream=None):
     """fp32 forward: returns (O fp32, lse fp32)."""
-    import torch
-
-    B, H, N, d = _shape(q)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    (B, H, N, d), out, lse = _fwd_args("fwd_f32", q, k, v, blockmask, out, lse, "f32")
     _check(fa_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, float(scale),
                       int(causal), _ptr(blockmask), _stream(stream)), "fa_fwd_f32")
     return out, lse
@@ -313,17 +406,11 @@ def fwd_f32(q, k, v, scale, causal=False, blockmask=None, out=None, lse=None, st
 def bwd_f32(q, k, v, o, lse, dout, scale, causal=False, blockmask=None, grads=None,
             workspace=None, stream=None):
     """fp32 backward: returns (dQ, dK, dV), fp32."""
-    import torch
-
     B, H, N, d = _shape(q)
-    if grads is None:
-        grads = tuple(torch.empty_like(q) for _ in range(3))
-    dq, dk, dv = grads
-    wsb = fa_bwd_workspace_bytes(B, H, N, d)
-    if workspace is None:
-        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=q.device)
+    (B, H, N, d), (dq, dk, dv), workspace = _bwd_args(
+        "bwd_f32", q, k, v, o, lse, dout, blockmask, grads, workspace, "f32",
+        fa_bwd_workspace_bytes(B, H, N, d))
     _check(fa_bwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
                       _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(causal), _ptr(blockmask),
-                      _ptr(workspace), workspace.numel() * workspace.element_size(),
-                      _stream(stream)), "fa_bwd_f32")
+                      _ptr(workspace), _nbytes(workspace), _stream(stream)), "fa_bwd_f32")
     return dq, dk, dv

@@ -120,13 +120,13 @@ __device__ __forceinline__ int xcd_remap(int g, int total) {
 // Users therefore wait for these copies themselves (s_waitcnt vmcnt(0), then
 // a barrier) before any wave reads the destination; the compiler's own vmcnt
 // waits for other loads can only become longer (completions are in order),
-// never too short.
+// never too short.  The LDS address goes in M0 as an input operand ("{m0}"),
+// so the compiler writes M0 itself and knows the statement reads it and leaves
+// it unchanged; the s_nop is the wait state between an M0 write and a copy
+// that reads it.
 __device__ __forceinline__ void lds_dma16_untracked(const void* src, char* lds) {
   const uint32_t m = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(src), "s"(m)
-               : "memory", "m0");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(m) : "memory");
 }
 
 // Direct-to-LDS copy of ROWS consecutive rows of a [N][D] bf16 matrix into

@@ -2,6 +2,9 @@
 the fp64 CPU oracle on the same seeded inputs)."""
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -43,20 +46,102 @@ def check(name, got, ref, dtype, report):
     assert e <= TOL[dtype][name], f"{name}: max-abs error {e:.3e} > {TOL[dtype][name]:.1e} ({report})"
 
 
+# ---- outputs with guard bands ---------------------------------------------------
+# Every output and workspace the tests hand to the library is a view into a
+# larger buffer: GUARD elements before and after it, all of it filled with a
+# NaN bit pattern first.  After the call every guard element must still hold
+# that exact pattern (no store outside the tensor) and no element of the
+# tensor may be NaN (every element written; the inputs are finite, so a
+# correct kernel never produces NaN).
+GUARD = 128 * 128
+_NAN_BITS = {torch.bfloat16: (torch.int16, 0x7FC1), torch.float32: (torch.int32, 0x7FC00001)}
+
+
+class Guarded:
+    def __init__(self, shape, dtype, dev):
+        self.shape = tuple(int(s) for s in shape)
+        self.n = int(np.prod(self.shape)) if self.shape else 1
+        self.dtype = dtype
+        ity, bits = _NAN_BITS[dtype]
+        self.full = torch.empty(self.n + 2 * GUARD, dtype=dtype, device=dev)
+        self.full.view(ity).fill_(bits)
+        self.view = self.full[GUARD:GUARD + self.n].view(self.shape)
+
+    def check(self, name, interior=True):
+        """Guards untouched; with interior=True, no NaN left in the tensor."""
+        ity, bits = _NAN_BITS[self.dtype]
+        raw = self.full.view(ity)
+        front, back = raw[:GUARD], raw[GUARD + self.n:]
+        assert bool((front == bits).all()), f"{name}: a store landed in the guard before the tensor"
+        assert bool((back == bits).all()), f"{name}: a store landed in the guard after the tensor"
+        if interior:
+            nan = torch.isnan(self.view)
+            assert not bool(nan.any()), (f"{name}: {int(nan.sum())} elements not written (or NaN), "
+                                         f"first at {tuple(torch.nonzero(nan)[0].tolist())}")
+
+
+def guarded_workspace(nbytes, dev):
+    return Guarded(((max(int(nbytes), 4) + 3) // 4,), torch.float32, dev)
+
+
 def run_gpu(q, k, v, do, scale, causal, mask, dtype, dev, backward=True):
-    """Forward (+ backward) on the GPU; returns CPU tensors."""
+    """Forward (+ backward) on the GPU into guarded, NaN-prefilled outputs;
+    checks the guards and that every output element was written; returns CPU
+    tensors."""
     import exact_io_aware_18_amd as fa
 
     qg, kg, vg, dog = (t.to(dev) for t in (q, k, v, do))
     mg = None if mask is None else mask.to(dev)
+    B, H, N, d = q.shape
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    o = Guarded(q.shape, tdt, dev)
+    lse = Guarded((B, H, N), torch.float32, dev)
+    grads = None
     if dtype == "bf16":
-        o, lse = fa.fwd(qg, kg, vg, scale, causal, mg)
-        grads = fa.bwd(qg, kg, vg, o, lse, dog, scale, causal, mg) if backward else None
+        fa.fwd(qg, kg, vg, scale, causal, mg, out=o.view, lse=lse.view)
     else:
-        o, lse = fa.fwd_f32(qg, kg, vg, scale, causal, mg)
-        grads = fa.bwd_f32(qg, kg, vg, o, lse, dog, scale, causal, mg) if backward else None
+        fa.fwd_f32(qg, kg, vg, scale, causal, mg, out=o.view, lse=lse.view)
+    if backward:
+        grads = [Guarded(q.shape, torch.float32, dev) for _ in range(3)]
+        ws = guarded_workspace(fa.fa_bwd_workspace_bytes(B, H, N, d), dev)
+        bwd = fa.bwd if dtype == "bf16" else fa.bwd_f32
+        bwd(qg, kg, vg, o.view, lse.view, dog, scale, causal, mg,
+            grads=tuple(g.view for g in grads), workspace=ws.view)
     torch.cuda.synchronize()
-    out = {"o": o.cpu(), "lse": lse.cpu()}
+    o.check("o")
+    lse.check("lse")
+    out = {"o": o.view.cpu(), "lse": lse.view.cpu()}
     if grads is not None:
-        out.update(dq=grads[0].cpu(), dk=grads[1].cpu(), dv=grads[2].cpu())
+        ws.check("workspace", interior=False)
+        for name, g in zip(("dq", "dk", "dv"), grads):
+            g.check(name)
+            out[name] = g.view.cpu()
+    return out
+
+
+# ---- the oracle over many heads ------------------------------------------------
+def oracle_threads():
+    """Worker threads for per-head oracle work: the CPUs this process may use,
+    at most 16 (the host share of one GPU)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def per_head(fn, heads, progress=None):
+    """fn(b, h) for every (b, h) in `heads` on a thread pool (numpy releases
+    the GIL in its array loops); BLAS is held to one thread per worker.
+    Returns {(b, h): result}."""
+    from threadpoolctl import threadpool_limits
+
+    out = {}
+    with threadpool_limits(limits=1):
+        with ThreadPoolExecutor(oracle_threads()) as ex:
+            futs = {ex.submit(fn, b, h): (b, h) for b, h in heads}
+            for n_done, f in enumerate(futs, 1):
+                out[futs[f]] = f.result()
+                if progress:
+                    print(f"[{progress}] oracle head {futs[f]} done ({n_done}/{len(heads)})", flush=True)
     return out

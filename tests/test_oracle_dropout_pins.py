@@ -1,13 +1,19 @@
 """Pins for the dropout oracle (oracle/dropout.py).
 
 The generator is pinned by the published known-answer vectors of
-Philox-4x32-10; the keep rule by its exact threshold arithmetic and by the
-binomial statistics of the mask; the forward by p = 0 reducing to plain
-attention and by unbiasedness over seeds (inverted dropout has E[O] equal to
-the dropout-free O); the backward by central finite differences of
-L = sum(dO * O) at a fixed seed and by the dK column-sum invariant.  A dropped
-1/(1-p) factor, a mask applied to the wrong operand, a mask missing from dP or
-a transposed (i, j) in the counter each fail one of these.
+Philox-4x32-10.  The keep rule is pinned by the first vector too: at seed 0
+the words Philox returns for counter (0, 0, 0, 0) are the ones compared with
+the threshold for query 0, keys 0..3 of head 0, so three thresholds between
+those four words fix which word serves which key.  The placement of the key
+group, query and head in the counter is checked against the layout the C
+header documents, at coordinates where a transposed (i, j), or head and query
+exchanged, gives a different mask.  Then the threshold arithmetic, the
+binomial statistics of the mask, p = 0 reducing to plain attention,
+unbiasedness over seeds (inverted dropout has E[O] equal to the dropout-free
+O), central finite differences of L = sum(dO * O) at a fixed seed and the dK
+column-sum invariant pin the rest.  A dropped 1/(1-p) factor, a mask applied
+to the wrong operand, a mask missing from dP, a permuted word order or a
+transposed (i, j) in the counter each fail one of these.
 """
 import json
 import os
@@ -39,6 +45,58 @@ def test_philox_known_answers():
         key = tuple(int(x, 16) for x in vec["key"])
         out = philox4x32_10(ctr, key)
         assert [int(x) for x in out] == [int(x, 16) for x in vec["out"]]
+
+
+def _kat():
+    g = json.load(open(os.path.join(GOLDEN, "philox4x32_10_kat.json")))
+    return g["vectors"]
+
+
+def test_keep_rule_known_answers():
+    """Query 0, keys 0..3, head 0, seed 0 use counter (0, 0, 0, 0) under key
+    (0, 0), the first published vector: key j takes word j, kept when the
+    word is at least floor(p * 2^32).  The four words lie in the order
+    w0 < w3 < w2 < w1, and p = 0.5, 0.7, 0.85 put a threshold in each gap, so
+    the three patterns fix the word of every key."""
+    vec = _kat()[0]
+    assert vec["counter"] == ["00000000"] * 4 and vec["key"] == ["00000000"] * 2
+    words = [int(x, 16) for x in vec["out"]]
+    patterns = {}
+    for p in (0.5, 0.7, 0.85):
+        T = int(np.floor(float(np.float32(p)) * 2.0**32))
+        expected = [w >= T for w in words]
+        got = keep_mask(0, np.array([0]), np.arange(4), p, seed=0)[0].tolist()
+        assert got == expected, (p, got, expected)
+        patterns[p] = tuple(expected)
+    assert patterns == {0.5: (False, True, True, True), 0.7: (False, True, True, False),
+                        0.85: (False, True, False, False)}
+
+
+def _documented_keep(bh, i, j, p, seed):
+    """The layout the C header states: word (j mod 4) of Philox-4x32-10 at
+    counter (j / 4, i, b*H + h, 0) and key (seed mod 2^32, seed / 2^32)."""
+    w = philox4x32_10(np.array([j // 4, i, bh, 0], dtype=np.uint64),
+                      (seed & 0xFFFFFFFF, seed >> 32))[j % 4]
+    return int(w) >= drop_threshold(p)
+
+
+def test_keep_rule_counter_layout():
+    """keep_mask against the documented layout at random coordinates, and the
+    same coordinates distinguish that layout from a transposed (i, j) and from
+    head and query exchanged."""
+    r = np.random.default_rng(77)
+    p, seed = 0.5, (3 << 32) + 12345
+    n_transposed = n_swapped = 0
+    for _ in range(300):
+        bh, i, j = (int(x) for x in r.integers(0, 5000, size=3))
+        z = keep_mask(bh, np.array([i]), np.array([j]), p, seed)[0, 0]
+        assert bool(z) == _documented_keep(bh, i, j, p, seed), (bh, i, j)
+        n_transposed += bool(z) != _documented_keep(bh, j, i, p, seed)
+        w = philox4x32_10(np.array([j // 4, bh, i, 0], dtype=np.uint64),
+                          (seed & 0xFFFFFFFF, seed >> 32))[j % 4]
+        n_swapped += bool(z) != (int(w) >= drop_threshold(p))
+    # independent fair coins disagree about half the time
+    assert 100 < n_transposed < 200 and 100 < n_swapped < 200
 
 
 def test_philox_batched_equals_single():

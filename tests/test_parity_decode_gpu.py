@@ -6,7 +6,7 @@ import torch
 
 from exact_io_aware_18_amd.inputs import default_scale, make_qkvdo
 from oracle.decode import attention_fwd_decode
-from tests.gpu_helpers import check, device, to64
+from tests.gpu_helpers import Guarded, check, device, guarded_workspace, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -27,8 +27,16 @@ def parity(B, H, Nq, Nk, d, causal, seed=0, scale=None):
     q, k, v = qkv(B, H, Nq, Nk, d, seed)
     print(f"\n[decode] B={B} H={H} Nq={Nq} Nk={Nk} d={d} causal={causal} "
           f"workspace={fa.fa_decode_workspace_bytes(B, H, Nq, Nk, d)}", flush=True)
-    o, lse = fa.decode(q.to(dev), k.to(dev), v.to(dev), scale, causal)
+    og = Guarded(q.shape, torch.bfloat16, dev)
+    lg = Guarded((B, H, Nq), torch.float32, dev)
+    ws = guarded_workspace(fa.fa_decode_workspace_bytes(B, H, Nq, Nk, d), dev)
+    fa.decode(q.to(dev), k.to(dev), v.to(dev), scale, causal, out=og.view, lse=lg.view,
+              workspace=ws.view)
     torch.cuda.synchronize()
+    og.check("o")
+    lg.check("lse")
+    ws.check("workspace", interior=False)
+    o, lse = og.view, lg.view
     o_ref, lse_ref = attention_fwd_decode(to64(q), to64(k), to64(v), scale, causal)
     rep = {}
     check("o", to64(o), o_ref, "bf16", rep)

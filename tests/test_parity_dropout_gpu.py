@@ -11,7 +11,7 @@ import torch
 
 from exact_io_aware_18_amd.inputs import default_scale, make_blockmask, make_qkvdo, workload_inputs
 from oracle.dropout import attention_bwd_dropout, attention_fwd_dropout, keep_mask
-from tests.gpu_helpers import check, device, to64
+from tests.gpu_helpers import Guarded, check, device, guarded_workspace, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -19,17 +19,28 @@ SEED = (1 << 40) + 123
 
 
 def run_drop(q, k, v, do, scale, causal, mask, p, seed, dev, backward=True):
+    """Dropout forward (+ backward) into guarded, NaN-prefilled outputs."""
     import exact_io_aware_18_amd as fa
 
     qg, kg, vg, dog = (t.to(dev) for t in (q, k, v, do))
     mg = None if mask is None else mask.to(dev)
-    o, lse = fa.fwd_dropout(qg, kg, vg, scale, p, seed, causal, mg)
-    out = {"o": o, "lse": lse}
+    B, H, N, d = q.shape
+    o = Guarded(q.shape, torch.bfloat16, dev)
+    lse = Guarded((B, H, N), torch.float32, dev)
+    fa.fwd_dropout(qg, kg, vg, scale, p, seed, causal, mg, out=o.view, lse=lse.view)
+    guards = {"o": o, "lse": lse}
     if backward:
-        out["dq"], out["dk"], out["dv"] = fa.bwd_dropout(qg, kg, vg, o, lse, dog, scale, p, seed,
-                                                         causal, mg)
+        grads = [Guarded(q.shape, torch.float32, dev) for _ in range(3)]
+        ws = guarded_workspace(fa.fa_bwd_workspace_bytes(B, H, N, d), dev)
+        fa.bwd_dropout(qg, kg, vg, o.view, lse.view, dog, scale, p, seed, causal, mg,
+                       grads=tuple(g.view for g in grads), workspace=ws.view)
+        guards.update(dq=grads[0], dk=grads[1], dv=grads[2])
     torch.cuda.synchronize()
-    return {k_: v_.cpu() for k_, v_ in out.items()}
+    for name, g in guards.items():
+        g.check(name)
+    if backward:
+        ws.check("workspace", interior=False)
+    return {name: g.view.cpu() for name, g in guards.items()}
 
 
 def parity(q, k, v, do, scale, causal, mask, p, seed):
