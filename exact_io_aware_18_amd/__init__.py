@@ -6,7 +6,7 @@ memory and the current stream.  If the shared library is missing, every call
 raises; there is no fallback implementation.
 
 Low level: one function per exported symbol (fa_fwd, fa_bwd, the three
-backward stages, fa_fwd_dropout, fa_bwd_dropout, fa_fwd_decode,
+backward stages, fa_bwd_noalloc, fa_bwd_noalloc_max_rows, fa_fwd_dropout, fa_bwd_dropout, fa_fwd_decode,
 fa_decode_workspace_bytes, fa_fwd_f32, fa_bwd_f32, fa_bwd_workspace_bytes,
 fa_fwd_query_rows, fa_strerror, fa_version) takes the C arguments as they are (pointers as
 integers).  High level: fwd, bwd, bwd_stages, fwd_dropout, bwd_dropout,
@@ -26,8 +26,9 @@ STATUS_NAMES = {
     0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_SHAPE", -3: "FA_ERR_HEADDIM",
     -4: "FA_ERR_ALIGN", -5: "FA_ERR_ALIAS", -6: "FA_ERR_WORKSPACE", -7: "FA_ERR_FLAG",
     -8: "FA_ERR_LAUNCH", -9: "FA_ERR_UNSUPPORTED", -10: "FA_ERR_SCALE", -11: "FA_ERR_DROPOUT",
+    -12: "FA_ERR_SCRATCH",
 }
-EXPORTED = ("fa_fwd", "fa_bwd", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq",
+EXPORTED = ("fa_fwd", "fa_bwd", "fa_bwd_noalloc", "fa_bwd_noalloc_max_rows", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq",
             "fa_fwd_dropout", "fa_bwd_dropout", "fa_fwd_decode", "fa_decode_workspace_bytes",
             "fa_bwd_workspace_bytes", "fa_fwd_query_rows", "fa_fwd_f32",
             "fa_bwd_f32", "fa_strerror", "fa_version")
@@ -54,6 +55,10 @@ def lib() -> ctypes.CDLL:
         L.fa_fwd.restype = I
         L.fa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, Z, P]
         L.fa_bwd.restype = I
+        L.fa_bwd_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, F, I, P, P]
+        L.fa_bwd_noalloc.restype = I
+        L.fa_bwd_noalloc_max_rows.argtypes = []
+        L.fa_bwd_noalloc_max_rows.restype = Z
         L.fa_bwd_preprocess.argtypes = [P, P, I, I, I, I, P, Z, P]
         L.fa_bwd_preprocess.restype = I
         L.fa_bwd_dkdv.argtypes = [P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, Z, P]
@@ -93,6 +98,16 @@ def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, blockma
            workspace, workspace_bytes, stream) -> int:
     return lib().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal,
                         blockmask, workspace, workspace_bytes, stream)
+
+
+def fa_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, blockmask,
+                   stream) -> int:
+    return lib().fa_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal,
+                                blockmask, stream)
+
+
+def fa_bwd_noalloc_max_rows() -> int:
+    return lib().fa_bwd_noalloc_max_rows()
 
 
 def fa_bwd_preprocess(o, dout, B, H, N, d, workspace, workspace_bytes, stream) -> int:
@@ -258,7 +273,8 @@ def _fwd_args(where, q, k, v, blockmask, out, lse, kind):
     return shp, out, lse
 
 
-def _bwd_args(where, q, k, v, o, lse, dout, blockmask, grads, workspace, kind, ws_bytes):
+def _bwd_args(where, q, k, v, o, lse, dout, blockmask, grads, workspace, kind, ws_bytes,
+              need_ws=True):
     """Validate a backward call; allocate the gradients and the workspace
     when not given."""
     import torch
@@ -284,7 +300,7 @@ def _bwd_args(where, q, k, v, o, lse, dout, blockmask, grads, workspace, kind, w
     dev = a.devices()
     if grads is None:
         grads = tuple(torch.empty(shp, dtype=torch.float32, device=dev) for _ in range(3))
-    if workspace is None:
+    if workspace is None and need_ws:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     return shp, grads, workspace
 
@@ -311,6 +327,20 @@ def bwd(q, k, v, o, lse, dout, scale, causal=False, blockmask=None, grads=None,
     _check(fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
                   _ptr(dv), B, H, N, d, float(scale), int(causal), _ptr(blockmask),
                   _ptr(workspace), _nbytes(workspace), _stream(stream)), "fa_bwd")
+    return dq, dk, dv
+
+
+def bwd_noalloc(q, k, v, o, lse, dout, scale, causal=False, blockmask=None, grads=None,
+                stream=None):
+    """bf16 backward through fa_bwd_noalloc (no workspace; D in the library's
+    fixed per-GPU array).  Returns (dQ, dK, dV), fp32 [B,H,N,d]; with grads
+    given, nothing is allocated here either."""
+    B, H, N, d = _shape(q)
+    (B, H, N, d), (dq, dk, dv), _ = _bwd_args(
+        "bwd_noalloc", q, k, v, o, lse, dout, blockmask, grads, None, "bf16", 0, need_ws=False)
+    _check(fa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                          _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(causal),
+                          _ptr(blockmask), _stream(stream)), "fa_bwd_noalloc")
     return dq, dk, dv
 
 

@@ -6,6 +6,7 @@
 #include <cfloat>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "fa.h"
 #include "fa_bwd.h"
@@ -386,6 +387,35 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, in
   return launched();
 }
 
+// ---- backward without a caller workspace ------------------------------------
+// fa_bwd_noalloc keeps the per-row D of the backward in this file-scope device
+// array instead of a caller workspace.  Every GPU the library runs on holds
+// its own copy, from the first use until the process ends.  Host code must
+// not pass `scratch` itself to a kernel (on the host it names a stand-in, not
+// the device array): the device address comes from hipGetSymbolAddress, taken
+// once per device with that device current, and is kept below.
+constexpr size_t kScratchFloats = size_t(1) << 22;  // 16 MiB: B * H * N <= 4,194,304
+static __device__ __align__(256) float scratch[kScratchFloats];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up on the first
+// call on that device.
+int scratch_on_current_device(float** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FA_ERR_LAUNCH;
+    g_scratch_ptr[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -419,6 +449,26 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
   const fa::BwdArgs a = bwd_args(q, k, v, o, lse, dout, dq, dk, dv, N, scale, blockmask, workspace);
   return run_bwd(a, B * H, d, causal, blockmask != nullptr, kPre | kDkdv | kDq, stream);
 }
+
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, float* dq, float* dk, float* dv, int B, int H, int N, int d,
+                   float scale, int causal, const unsigned char* blockmask, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dout) return FA_ERR_NULL;
+  int st = check_common(B, H, N, d, scale, causal);
+  if (st) return st;
+  if ((size_t)B * H * N > kScratchFloats) return FA_ERR_SCRATCH;
+  const Sizes z = sizes(B, H, N, d, 2);
+  const Buf ins[7] = {{q, z.t, 16}, {k, z.t, 16}, {v, z.t, 16}, {o, z.t, 16},
+                      {dout, z.t, 16}, {lse, z.l, 4}, {blockmask, z.m, 1}};
+  const Buf outs[3] = {{dq, z.g, 16}, {dk, z.g, 16}, {dv, z.g, 16}};
+  if ((st = check_bufs(ins, 7, outs, 3))) return st;
+  float* ws = nullptr;
+  if ((st = scratch_on_current_device(&ws))) return st;
+  const fa::BwdArgs a = bwd_args(q, k, v, o, lse, dout, dq, dk, dv, N, scale, blockmask, ws);
+  return run_bwd(a, B * H, d, causal, blockmask != nullptr, kPre | kDkdv | kDq, stream);
+}
+
+size_t fa_bwd_noalloc_max_rows(void) { return kScratchFloats; }
 
 int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const float* lse,
                    const void* dout, float* dq, float* dk, float* dv, int B, int H, int N, int d,
@@ -602,10 +652,11 @@ const char* fa_strerror(int status) {
     case FA_ERR_ALIAS: return "an output overlaps an input or another output";
     case FA_ERR_WORKSPACE: return "workspace is NULL or smaller than fa_bwd_workspace_bytes()";
     case FA_ERR_FLAG: return "causal must be 0 or 1";
-    case FA_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
+    case FA_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch or a runtime query";
     case FA_ERR_UNSUPPORTED: return "arguments are valid but not supported by this build";
     case FA_ERR_SCALE: return "scale must be finite";
     case FA_ERR_DROPOUT: return "dropout probability must be in [0, 1)";
+    case FA_ERR_SCRATCH: return "B * H * N exceeds fa_bwd_noalloc_max_rows()";
     default: return "unknown status";
   }
 }

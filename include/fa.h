@@ -28,7 +28,8 @@
  *     block covers the remainder when N % 128 != 0.  causal and blockmask
  *     combine by AND.
  *   - Ownership: every pointer is caller-owned device memory.  The library
- *     allocates nothing, frees nothing and keeps no state, so concurrent
+ *     allocates nothing and frees nothing.  Apart from fa_bwd_noalloc (a
+ *     fixed per-GPU device array, see there) it keeps no state, so concurrent
  *     calls on different streams are safe.  Inputs are only read; outputs
  *     are fully overwritten.
  *   - Asynchrony: work is enqueued on `stream` (a hipStream_t, NULL = the
@@ -60,10 +61,11 @@ typedef enum {
     FA_ERR_ALIAS = -5,       /* an output overlaps an input or another output */
     FA_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than fa_bwd_workspace_bytes() */
     FA_ERR_FLAG = -7,        /* causal is not 0 or 1 */
-    FA_ERR_LAUNCH = -8,      /* the HIP runtime rejected a kernel launch */
+    FA_ERR_LAUNCH = -8,      /* the HIP runtime rejected a launch or a query */
     FA_ERR_UNSUPPORTED = -9, /* valid arguments this build does not handle */
     FA_ERR_SCALE = -10,      /* scale is NaN or infinite */
-    FA_ERR_DROPOUT = -11     /* p_drop is NaN or outside [0, 1) */
+    FA_ERR_DROPOUT = -11,    /* p_drop is NaN or outside [0, 1) */
+    FA_ERR_SCRATCH = -12     /* B*H*N exceeds fa_bwd_noalloc_max_rows() */
 } fa_status;
 
 /*
@@ -90,6 +92,28 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            int B, int H, int N, int d, float scale, int causal,
            const unsigned char* blockmask, void* workspace,
            size_t workspace_bytes, void* stream);
+
+/*
+ * fa_bwd without the workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops, harnesses that
+ * forbid hipMalloc).  The per-row D that fa_bwd keeps in the caller's
+ * workspace lives instead in a fixed device array inside the library, one
+ * per GPU, held from the first call on that GPU until the process ends
+ * (16 MiB: B * H * N <= fa_bwd_noalloc_max_rows() = 4,194,304, else
+ * FA_ERR_SCRATCH before any HIP call).  The call allocates and frees nothing.
+ * Every call on one GPU shares that array: calls on one GPU that overlap in
+ * time (different streams, or host threads without ordering) race on it and
+ * must be serialised by the caller.  Other arguments, results and errors as
+ * for fa_bwd; the first call on a device also queries the array's address
+ * (FA_ERR_LAUNCH if the runtime refuses).
+ */
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                   const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                   int B, int H, int N, int d, float scale, int causal,
+                   const unsigned char* blockmask, void* stream);
+
+/* Largest B * H * N fa_bwd_noalloc accepts. */
+size_t fa_bwd_noalloc_max_rows(void);
 
 /*
  * The three stages fa_bwd runs, in this order, as separate calls (bf16 path)

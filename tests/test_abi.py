@@ -301,3 +301,38 @@ def test_header_is_plain_c(compiler, lang, std, tmp_path):
                           if lang == "c" else "-Wall", "-fsyntax-only", "-I",
                           os.path.join(ROOT, "include"), str(src)], capture_output=True, text=True)
     assert out.returncode == 0, out.stderr
+
+
+def call_noalloc(a):
+    return fa.fa_bwd_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dout"], a["dq"], a["dk"],
+                             a["dv"], a["B"], a["H"], a["N"], a["d"], a["scale"], a["causal"],
+                             a["blockmask"], a["stream"])
+
+
+def test_noalloc_limit(lib):
+    assert fa.fa_bwd_noalloc_max_rows() == 1 << 22
+    assert fa.fa_strerror(-12).startswith("B * H * N exceeds")
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(dout=None), -1), (dict(o=None), -1), (dict(lse=None), -1),
+    (dict(N=0), -2), (dict(d=80), -3),
+    (dict(dk=BASE + 7 * (256 * 64 * 2 * 4 + MB) + 4), -4),
+    (dict(causal=3), -7), (dict(scale=float("nan")), -10),
+])
+def test_noalloc_rejects(lib, over, code):
+    a = bwd_args()
+    a.update(over)
+    assert call_noalloc(a) == code
+
+
+def test_noalloc_rejects_aliasing_and_size(lib):
+    a = bwd_args()
+    assert call_noalloc(dict(a, dq=a["q"])) == -5
+    assert call_noalloc(dict(a, dv=a["dk"] + 64)) == -5
+    # one row past the fixed array: rejected before any HIP call
+    big = bwd_args(B=1, H=64, N=65537)
+    assert call_noalloc(big) == -12
+    ok = bwd_args(B=1, H=64, N=65536)  # exactly the limit passes the size check
+    assert 64 * 65536 == fa.fa_bwd_noalloc_max_rows()
+    assert call_noalloc(dict(ok, dq=ok["q"])) == -5  # ... and reaches the alias check
