@@ -72,9 +72,9 @@ def pairs_per_head(N, causal, mask):
     return total
 
 
-def load_traffic(kernel_key: str):
-    """HBM bytes per launch from the committed counter summary, if it was taken
-    on the current kernel sources; else None."""
+def load_traffic(workload: str, kernel_key: str):
+    """HBM bytes per launch of one kernel of a workload, from the committed
+    counter summary, if it was taken on the current kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -82,11 +82,12 @@ def load_traffic(kernel_key: str):
         rec = json.load(f)
     if rec.get("source_hash") != kernel_source_hash():
         return None
-    ent = rec.get("kernels", {}).get(kernel_key)
+    ent = rec.get("workloads", {}).get(workload, {}).get("kernels", {}).get(kernel_key)
     return None if ent is None else ent.get("hbm_bytes_per_launch")
 
 
-CPU_SAMPLE_HEADS = 4
+CPU_BUDGET_S = 15.0  # host time for the oracle sample
+CPU_MAX_HEADS = 64
 COLD_FLUSH_BYTES = 512 << 20  # written between cold steps: twice the 256 MB last-level cache
 
 
@@ -152,9 +153,23 @@ class ClockSampler:
                 "source": "pp_dpm_sclk"}
 
 
-def cpu_baseline(sub_names):
-    """The fp64 oracle, as it stands, on CPU_SAMPLE_HEADS heads of each
-    sub-workload (full forward and backward), timed on this host's cores."""
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(sub_names, budget_s=CPU_BUDGET_S):
+    """The fp64 oracle, as it stands, timed on this host's cores: full forward
+    and backward of whole heads of each sub-workload, one head after another
+    until the sub-workload's share of the time budget is spent (at least one
+    head, at most CPU_MAX_HEADS)."""
     import numpy as np
 
     from exact_io_aware_18_amd.inputs import WORKLOADS, default_scale, make_blockmask, make_qkvdo
@@ -172,23 +187,31 @@ def cpu_baseline(sub_names):
     for name in sub_names:
         w = WORKLOADS[name]
         N, d = w["N"], w["d"]
-        q, k, v, do = make_qkvdo(1, CPU_SAMPLE_HEADS, N, d, w["dtype"], seed=0)
+        heads = min(CPU_MAX_HEADS, w["B"] * w["H"])
+        q, k, v, do = make_qkvdo(1, heads, N, d, w["dtype"], seed=0)
         mask = make_blockmask(N, w.get("frac", 0.125)) if w["mask"] else None
         m = None if mask is None else mask.numpy()
         q64, k64, v64, do64 = (t.double().numpy() for t in (q, k, v, do))
-        t0 = time.perf_counter()
-        attention_fwd(q64, k64, v64, default_scale(d), w["causal"], m)
-        attention_bwd(q64, k64, v64, do64, default_scale(d), w["causal"], m)
-        secs += time.perf_counter() - t0
-        flops += 14.0 * d * pairs_per_head(N, w["causal"], mask) * CPU_SAMPLE_HEADS
-        desc.append(f"{name}: B=1 H={CPU_SAMPLE_HEADS} N={N} d={d}")
+        used, t_sub = 0, 0.0
+        while used < heads and (used == 0 or t_sub < budget_s / len(sub_names)):
+            sl = (slice(0, 1), slice(used, used + 1))
+            t0 = time.perf_counter()
+            attention_fwd(q64[sl], k64[sl], v64[sl], default_scale(d), w["causal"], m)
+            attention_bwd(q64[sl], k64[sl], v64[sl], do64[sl], default_scale(d), w["causal"], m)
+            t_sub += time.perf_counter() - t0
+            used += 1
+        secs += t_sub
+        flops += 14.0 * d * pairs_per_head(N, w["causal"], mask) * used
+        desc.append(f"{name}: {used} head(s) of N={N} d={d}")
     return {
         "value": flops / secs / 1e12,
         "unit": "TFLOP/s",
         "cores": cores,
+        "cpu_model": cpu_model(),
         "kind": "oracle",
-        "sample": f"full fp64 forward+backward of {CPU_SAMPLE_HEADS} heads of each sub-workload (" + "; ".join(desc)
-                  + f"), {secs:.1f} s",
+        "sample": "full fp64 forward+backward of whole heads, one after another until about "
+                  f"{budget_s:.0f} s are spent (" + "; ".join(desc) + f"), {secs:.1f} s; FLOP count "
+                  "14d per unmasked pair (the forward's 4d and the backward's 10d)",
     }
 
 
@@ -557,7 +580,8 @@ def main():
     else:
         achieved, peak, unit, bound = dk_["gbs"], PEAK_HBM_GBS, "GB/s", "hbm"
     roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-                "frac": round(achieved / peak, 4), "traffic": load_traffic(dom), "kernel": dom,
+                "frac": round(achieved / peak, 4),
+                "traffic": load_traffic(args.workload, dom) if drop == 0 else None, "kernel": dom,
                 "kernel_ms": round(dk_["ms"], 4)}
 
     # the same object for each forward kernel (the forward alone has its own
@@ -567,7 +591,7 @@ def main():
         if key.startswith(kinds[0] + "_d") and "tflops" in kv:
             roofline_fwd[key] = {"bound": "mfma", "achieved": round(kv["tflops"], 2), "peak": PEAK_BF16_TFLOPS,
                                  "unit": "TFLOP/s", "frac": round(kv["tflops"] / PEAK_BF16_TFLOPS, 4),
-                                 "traffic": load_traffic(key) if drop == 0 else None,
+                                 "traffic": load_traffic(args.workload, key) if drop == 0 else None,
                                  "kernel_ms": round(kv["ms"], 4)}
 
     out = {

@@ -42,6 +42,18 @@
  *     B * H * ceil(N/128) < 2^24; scale finite.
  *     Tensor pointers must be 16-byte aligned, lse 4-byte aligned.
  *     No output may overlap an input or another output.
+ *   - Accuracy.  Any finite scale is accepted; the error is that of the
+ *     arithmetic's precision, not of the scale.  bf16 path: products take
+ *     bf16 operands with fp32 accumulation; P (in O = P V and dV = P^T dO),
+ *     dS (in dQ and dK) and the returned O are rounded to bf16 (unit
+ *     roundoff 2^-8), and the backward's D = rowsum(dO o O) uses that bf16
+ *     O.  Errors therefore scale with the outputs: measured max-abs error of
+ *     O, dQ, dK and dV is at most 0.85% of the largest |element| of the same
+ *     tensor (N(0,1) inputs, |scale| up to 0.5, rows with 40-unit score
+ *     spreads), which is within 2e-2 absolute while |O|, |dQ|, |dK|, |dV|
+ *     stay below ~2.5 (N(0,1) inputs at scale 1/sqrt(d)).  lse is fp32
+ *     (error ~1e-6 of |lse|).  fp32 path: fp32 throughout, measured max-abs
+ *     error at most 3.2e-6 of the largest |element| (|scale| up to 1).
  */
 #ifndef FA_MI355X_FA_H
 #define FA_MI355X_FA_H

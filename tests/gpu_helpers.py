@@ -46,6 +46,26 @@ def check(name, got, ref, dtype, report):
     assert e <= TOL[dtype][name], f"{name}: max-abs error {e:.3e} > {TOL[dtype][name]:.1e} ({report})"
 
 
+# Accuracy envelope away from the workloads' scale (the C header states it):
+# the bf16 path rounds O, P and dS to bf16 (unit roundoff 2^-8), so its errors
+# grow with the outputs themselves; measured max-abs error / max |x| <= 0.85%.
+# Outside the workloads, O, dQ, dK and dV are held to the larger of the fixed
+# tolerance and REL[dtype] times the largest |element| of the reference tensor
+# (about twice the measured ratio).  lse keeps its absolute tolerance.
+REL = {"bf16": 2.0 ** -6, "f32": 2.0 ** -17}
+
+
+def check_envelope(name, got, ref, dtype, report):
+    ref = np.asarray(ref, dtype=np.float64)
+    fin = ref[np.isfinite(ref)]
+    mag = float(np.abs(fin).max()) if fin.size else 0.0
+    tol = TOL[dtype][name] if name == "lse" else max(TOL[dtype][name], REL[dtype] * mag)
+    e = maxerr(got, ref)
+    report[name] = e
+    report[name + "/max|x|"] = e / mag if mag else 0.0
+    assert e <= tol, f"{name}: max-abs error {e:.3e} > {tol:.2e} (max|x| {mag:.3g}; {report})"
+
+
 # ---- outputs with guard bands ---------------------------------------------------
 # Every output and workspace the tests hand to the library is a view into a
 # larger buffer: GUARD elements before and after it, all of it filled with a

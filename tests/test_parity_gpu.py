@@ -16,7 +16,7 @@ from exact_io_aware_18_amd.inputs import (
     workload_inputs,
 )
 from oracle import attention_bwd, attention_fwd, attention_fwd_rows
-from tests.gpu_helpers import TOL, check, device, maxerr, per_head, run_gpu, to64
+from tests.gpu_helpers import TOL, check, check_envelope, device, maxerr, per_head, run_gpu, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -141,14 +141,44 @@ def test_block_mask_with_empty_rows(dtype):
     assert torch.all(got["dq"][:, :, 128:256] == 0)
 
 
-# bf16 errors grow with |scale| (the rounding of P and dS is relative to
-# scores whose spread is scale * |q||k|), so the bf16 cases keep the
-# workloads' magnitude 1/sqrt(d); the fp32 path is checked at larger scales.
 @pytest.mark.parametrize("dtype,scale", [("bf16", -0.125), ("bf16", 0.0), ("f32", -0.3),
                                          ("f32", 0.0), ("f32", 0.25)])
 def test_other_scales(dtype, scale):
     q, k, v, do = make_qkvdo(1, 2, 300, 64, dtype, seed=8)
     full_parity(q, k, v, do, scale, True, None, dtype)
+
+
+def envelope_parity(q, k, v, do, scale, causal, dtype):
+    """Forward and backward against the oracle with the accuracy envelope of
+    the C header: max-abs error within the fixed tolerance or REL times the
+    largest |element| of the tensor, whichever is larger."""
+    dev = device()
+    print(f"\n[envelope] shape={tuple(q.shape)} dtype={dtype} causal={causal} scale={scale}", flush=True)
+    got = run_gpu(q, k, v, do, scale, causal, None, dtype, dev)
+    q64, k64, v64, do64 = (to64(t) for t in (q, k, v, do))
+    o_ref, lse_ref = attention_fwd(q64, k64, v64, scale, causal)
+    g_ref = attention_bwd(q64, k64, v64, do64, scale, causal)
+    rep = {}
+    for name, ref in zip(("o", "lse", "dq", "dk", "dv"), (o_ref, lse_ref) + tuple(g_ref)):
+        check_envelope(name, to64(got[name]), ref, dtype, rep)
+    print("[envelope]", {k_: f"{v_:.2e}" for k_, v_ in rep.items()}, flush=True)
+
+
+# Larger |scale| sharpens the softmax and grows dS and the gradients with it;
+# bf16 rounding of O, P and dS then exceeds 2e-2 absolute while staying a
+# fixed fraction of the outputs (a CPU model of that rounding alone, fed the
+# GPU's O and lse, reproduces the GPU's gradient errors to three digits).
+@pytest.mark.parametrize("dtype,shape,scale,causal", [
+    ("bf16", (1, 4, 1024, 64), -0.3, True),
+    ("bf16", (1, 4, 1024, 64), 0.5, True),
+    ("bf16", (1, 4, 512, 128), -0.3, False),
+    ("bf16", (2, 64, 1000, 64), 0.3, True),   # two-group forward kernel
+    ("f32", (1, 2, 300, 64), 0.5, True),
+    ("f32", (1, 2, 300, 128), 1.0, True),
+])
+def test_accuracy_envelope(dtype, shape, scale, causal):
+    q, k, v, do = make_qkvdo(*shape, dtype, seed=8)
+    envelope_parity(q, k, v, do, scale, causal, dtype)
 
 
 def test_f32_with_block_mask():
@@ -202,9 +232,10 @@ def test_row_shift_on_gpu():
 def test_running_max_moves_late(d, causal):
     """Scores that grow along the keys (key rows scaled by a ramp) and one
     planted dominant key late in the sequence: the reference max must move
-    in tiles after the first, through the forward's recompute path.  Forward
-    only: the backward reads lse and has no running max, and its bf16 error
-    on the 40-unit score row exceeds the fixed absolute tolerance."""
+    in tiles after the first, through the forward's recompute path.  The
+    forward is held to the fixed tolerance; forward and backward together to
+    the accuracy envelope (the backward's bf16 error on these sharp rows
+    reaches 2.4e-2 absolute, 0.7% of max |dQ|)."""
     N = 1100
     q, k, v, do = make_qkvdo(1, 2, N, d, "bf16", seed=31)
     ramp = torch.linspace(0.5, 2.0, N)[None, None, :, None]
@@ -213,6 +244,7 @@ def test_running_max_moves_late(d, causal):
     kk = k[0, 1, 650].float()
     q[0, 1, 700] = (kk * (40.0 / (kk.norm() ** 2 * default_scale(d)))).to(torch.bfloat16)
     full_parity(q, k, v, do, default_scale(d), causal, None, "bf16", backward=False)
+    envelope_parity(q, k, v, do, default_scale(d), causal, "bf16")
 
 
 @pytest.mark.parametrize("d", [64, 128])
