@@ -118,9 +118,14 @@ __global__ __launch_bounds__(256, DkdvTile<D>::MIN_WG) void bwd_dkdv_kernel(BwdA
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, li = lane & 31;
-  const int g = xcd_remap(blockIdx.x, a.total);
-  const int bh = g / a.ntile;
-  const int kt = g - bh * a.ntile;  // causal: low key tiles see the most queries, so they go first
+  int bh, kt;
+  if (CAUSAL) {  // low key tiles see the most queries: they go first, over all heads
+    causal_rank(blockIdx.x, a.total / a.ntile, bh, kt);
+  } else {
+    const int g = xcd_remap(blockIdx.x, a.total);
+    bh = g / a.ntile;
+    kt = g - bh * a.ntile;
+  }
   const int N = a.N;
   const size_t head = (size_t)bh * N * D;
   const int k0 = kt * BK;
@@ -373,9 +378,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
   const int pair = w & (T::NPAIR - 1);
   const bool ds_wave = w >= T::NPAIR;  // waves w and w + 4 share a SIMD
   const int h = lane >> 5, li = lane & 31;
-  const int g = xcd_remap(blockIdx.x, a.total);
-  const int bh = g / a.ntile;
-  const int kt = g - bh * a.ntile;
+  int bh, kt;
+  if (CAUSAL) {  // low key tiles see the most queries: they go first, over all heads
+    causal_rank(blockIdx.x, a.total / a.ntile, bh, kt);
+  } else {
+    const int g = xcd_remap(blockIdx.x, a.total);
+    bh = g / a.ntile;
+    kt = g - bh * a.ntile;
+  }
   const int N = a.N;
   const size_t head = (size_t)bh * N * D;
   const int k0 = kt * BK;
@@ -665,10 +675,15 @@ __global__ __launch_bounds__(256, DqTile<D>::MIN_WG) void bwd_dq_kernel(BwdArgs 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, li = lane & 31;
-  const int g = xcd_remap(blockIdx.x, a.total);
-  const int bh = g / a.ntile;
-  int qt = g - bh * a.ntile;
-  if (CAUSAL) qt = a.ntile - 1 - qt;
+  int bh, qt;
+  if (CAUSAL) {  // longest rows first, over all heads
+    causal_rank(blockIdx.x, a.total / a.ntile, bh, qt);
+    qt = a.ntile - 1 - qt;
+  } else {
+    const int g = xcd_remap(blockIdx.x, a.total);
+    bh = g / a.ntile;
+    qt = g - bh * a.ntile;
+  }
   const int N = a.N;
   const size_t head = (size_t)bh * N * D;
   const int q0 = qt * BR;

@@ -112,6 +112,19 @@ __device__ __forceinline__ int xcd_remap(int g, int total) {
   return (x < r) ? x * (q + 1) + s : r * (q + 1) + (x - r) * q + s;
 }
 
+// Causal tiles of a head differ in length (a query tile sees the keys up to
+// its diagonal).  Workgroup g takes length rank g / BH (0 = longest) of head
+// g % BH, so the grid runs longest first over all heads at once, the order
+// that keeps the end of the launch balanced; ordering each head's tiles on
+// its own left whole XCDs busy with the last heads' long tiles (GPT-2 shape:
+// 70K against 48K cycles, simulated with the measured per-tile cost).  With
+// BH a multiple of 8 the XCD of workgroup g (g % 8) still owns a fixed set of
+// heads, whose tiles then share its L2.
+__device__ __forceinline__ void causal_rank(int g, int BH, int& bh, int& rank) {
+  rank = g / BH;
+  bh = g - rank * BH;
+}
+
 // 16-byte direct-to-LDS copy (global_load_lds_dwordx4): lane l of the wave
 // writes its 16 bytes at lds + 16*l; lds must be wave-uniform.  Issued
 // through inline assembly so that the compiler does not track it: while it

@@ -114,10 +114,15 @@ __global__ __launch_bounds__(256, FwdTile<D>::MIN_WG) void fwd_bf16_kernel(FwdAr
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in an SGPR
   const int h = lane >> 5, li = lane & 31;
 
-  const int g = xcd_remap(blockIdx.x, a.total);
-  const int bh = g / a.nqt;
-  int qt = g - bh * a.nqt;
-  if (CAUSAL) qt = a.nqt - 1 - qt;  // longest rows first
+  int bh, qt;
+  if (CAUSAL) {  // longest rows first, over all heads
+    causal_rank(blockIdx.x, a.total / a.nqt, bh, qt);
+    qt = a.nqt - 1 - qt;
+  } else {
+    const int g = xcd_remap(blockIdx.x, a.total);
+    bh = g / a.nqt;
+    qt = g - bh * a.nqt;
+  }
   const int N = a.N;
   const size_t head = (size_t)bh * N * D;
   const __bf16* Qh = a.q + head;
@@ -428,10 +433,15 @@ __global__ __launch_bounds__(256 * G, 1) void fwd_pp_kernel(FwdArgs a) {
   const int grp = w >> 2;
   const int h = lane >> 5, li = lane & 31;
 
-  const int g = xcd_remap(blockIdx.x, a.total);
-  const int bh = g / a.nqt;
-  int qt = g - bh * a.nqt;
-  if (CAUSAL) qt = a.nqt - 1 - qt;  // longest rows first
+  int bh, qt;
+  if (CAUSAL) {  // longest rows first, over all heads
+    causal_rank(blockIdx.x, a.total / a.nqt, bh, qt);
+    qt = a.nqt - 1 - qt;
+  } else {
+    const int g = xcd_remap(blockIdx.x, a.total);
+    bh = g / a.nqt;
+    qt = g - bh * a.nqt;
+  }
   const int N = a.N;
   const size_t head = (size_t)bh * N * D;
   const __bf16* Qh = a.q + head;
