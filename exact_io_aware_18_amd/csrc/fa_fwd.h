@@ -383,13 +383,16 @@ __global__ __launch_bounds__(256, FwdTile<D>::MIN_WG) void fwd_bf16_kernel(FwdAr
 // SIMD w % 4, so every SIMD holds one wave of each group.  Per key tile a
 // wave does a matrix phase M (O^T += V^T P^T of the previous tile, then
 // S^T = K Q^T of this tile) and a vector phase (softmax of this tile's
-// scores).  Barriers split a round (one key tile) into G phases and hold the
-// groups one phase apart, so in every phase one wave per SIMD issues products
-// while the others run softmax.
+// scores).  The groups run one phase apart, so in every phase one wave per
+// SIMD issues products while the others run softmax.
 //
 // G = 2 (ping-pong): the vector phase is one step V.
 //   round r, phase 1:  A: M(r)      B: V(r-1)
 //   round r, phase 2:  A: V(r)      B: M(r)
+// Only the barrier at the end of a round (the copies have landed, the
+// buffers are free) holds the groups together: within a round the opposite
+// phase orders keep them apart, and a barrier between the two phases made
+// the round ~1.6% longer.
 // G = 3: a single wave issues VALU work at about half the rate a SIMD can
 // retire it (measured: two VALU-bound waves on one SIMD each run at the
 // speed of one alone), so the softmax is split into two steps V1 (mask, P and
@@ -399,6 +402,8 @@ __global__ __launch_bounds__(256, FwdTile<D>::MIN_WG) void fwd_bf16_kernel(FwdAr
 //   round r, phase 1:  A: M(r)      B: V2(r-1)   C: V1(r-1)
 //   round r, phase 2:  A: V1(r)     B: M(r)      C: V2(r-1)
 //   round r, phase 3:  A: V2(r)     B: V1(r)     C: M(r)
+// Here barriers split the round into its three phases (without them the
+// round is ~1.6% longer).
 // Round r reads K(r) and V(r-1); K(r+1) and V(r) are copied meanwhile into
 // the buffers round r-1 finished with.  Only group 0 issues the copies,
 // inside its matrix phase (K before the PV products, V between the PV and
@@ -630,7 +635,8 @@ __global__ __launch_bounds__(256 * G, 1) void fwd_pp_kernel(FwdArgs a) {
 
   // round r (r = 0 .. ntiles): K(r) in kb[r&1], V(r-1) in vb[(r-1)&1].
   // Each group runs its own loop (the phase order differs); all execute the
-  // same G barriers per round, the last after waiting for the copies.
+  // same barriers per round (one with G = 2, three with G = 3), the last
+  // after waiting for the copies.
   // mphase runs its last argument between the PV and the score products.
   // copies issued by group 0 (see the schedule above)
   auto copyk = [&] __device__ (int r, char* knext) __attribute__((always_inline)) {
@@ -655,7 +661,6 @@ __global__ __launch_bounds__(256 * G, 1) void fwd_pp_kernel(FwdArgs a) {
       rounds([&] __device__ (int r, const char* kcur, char* knext, const char* vprev, char* vcur) __attribute__((always_inline)) {
         copyk(r, knext);
         mphase(r, kcur, vprev, [&] __device__ () { copyv(r, vcur); });
-        __syncthreads();
         vstep1(r);
         vstep2(r);
         endround();
@@ -664,7 +669,6 @@ __global__ __launch_bounds__(256 * G, 1) void fwd_pp_kernel(FwdArgs a) {
       rounds([&] __device__ (int r, const char* kcur, char* knext, const char* vprev, char* vcur) __attribute__((always_inline)) {
         vstep1(r - 1);
         vstep2(r - 1);
-        __syncthreads();
         mphase(r, kcur, vprev, nomid);
         endround();
       });
