@@ -405,12 +405,13 @@ __global__ __launch_bounds__(256, FwdTile<D>::MIN_WG) void fwd_bf16_kernel(FwdAr
 // Here barriers split the round into its three phases (without them the
 // round is ~1.6% longer).
 // Round r reads K(r) and V(r-1); K(r+1) and V(r) are copied meanwhile into
-// the buffers round r-1 finished with.  Only group 0 issues the copies,
-// inside its matrix phase (K before the PV products, V between the PV and
-// score products): direct-to-LDS copies queue for the CU's address unit,
-// and a wave stalls while its copies issue, so issuing them from every wave
-// at the start of a round lengthened that round's first phase by ~300
-// cycles for all groups.
+// the buffers round r-1 finished with.  Direct-to-LDS copies queue for the
+// CU's address unit and a wave stalls while its copies issue, so issuing
+// them from every wave at the start of a round lengthened that round's first
+// phase by ~300 cycles for all groups.  Group 0 issues V inside its matrix
+// phase (between the PV and score products).  With G = 3 it also issues K,
+// before its PV products; with G = 2 group 1 issues K at the start of its
+// round, ahead of its vector phase (1-2% faster than group 0 issuing both).
 template <int D, int G = 2>
 struct FwdPPTile {
   static constexpr int NW = 4 * G;
@@ -467,7 +468,7 @@ __global__ __launch_bounds__(256 * G, 1) void fwd_pp_kernel(FwdArgs a) {
   TileOffsets<D> toff;
   toff.init(lane);
   TileCopy<BC, D, T::CPT> cp;
-  cp.init(w, lane);
+  cp.init(w & 3, lane);
   const bool copier = grp == 0;
 
   f32x16 o[NCT];
@@ -638,7 +639,8 @@ __global__ __launch_bounds__(256 * G, 1) void fwd_pp_kernel(FwdArgs a) {
   // same barriers per round (one with G = 2, three with G = 3), the last
   // after waiting for the copies.
   // mphase runs its last argument between the PV and the score products.
-  // copies issued by group 0 (see the schedule above)
+  // copies: see the schedule above; TileCopy covers 256 threads, so a
+  // wave copies as wave w & 3 of its group
   auto copyk = [&] __device__ (int r, char* knext) __attribute__((always_inline)) {
     if (copier && r + 1 < ntiles) cp.issue(knext, Kh, (r + 1) * BC, N, w);
   };
@@ -659,7 +661,6 @@ __global__ __launch_bounds__(256 * G, 1) void fwd_pp_kernel(FwdArgs a) {
   if constexpr (G == 2) {
     if (grp == 0) {
       rounds([&] __device__ (int r, const char* kcur, char* knext, const char* vprev, char* vcur) __attribute__((always_inline)) {
-        copyk(r, knext);
         mphase(r, kcur, vprev, [&] __device__ () { copyv(r, vcur); });
         vstep1(r);
         vstep2(r);
@@ -667,6 +668,7 @@ __global__ __launch_bounds__(256 * G, 1) void fwd_pp_kernel(FwdArgs a) {
       });
     } else {
       rounds([&] __device__ (int r, const char* kcur, char* knext, const char* vprev, char* vcur) __attribute__((always_inline)) {
+        if (r + 1 < ntiles) cp.issue(knext, Kh, (r + 1) * BC, N, w & 3);  // K(r+1)
         vstep1(r - 1);
         vstep2(r - 1);
         mphase(r, kcur, vprev, nomid);
