@@ -401,15 +401,22 @@ constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 float* g_scratch_ptr[kMaxDevices] = {};
 
-// Device address of `scratch` on the current device, looked up on the first
-// call on that device.
-int scratch_on_current_device(float** out) {
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_LAUNCH;
+// Device address of `scratch` on the GPU that runs stream s (the current GPU
+// for the default stream), looked up on the first call on that GPU with that
+// GPU current; the caller's current device is restored.
+int scratch_for_stream(hipStream_t s, float** out) {
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return FA_ERR_LAUNCH;
+  int dev = cur;
+  if (s && hipStreamGetDevice(s, &dev) != hipSuccess) return FA_ERR_LAUNCH;
+  if (dev < 0 || dev >= kMaxDevices) return FA_ERR_LAUNCH;
   std::lock_guard<std::mutex> lock(g_scratch_mu);
   if (!g_scratch_ptr[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return FA_ERR_LAUNCH;
     void* p = nullptr;
-    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FA_ERR_LAUNCH;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return FA_ERR_LAUNCH;
+    if (e != hipSuccess || !p) return FA_ERR_LAUNCH;
     g_scratch_ptr[dev] = static_cast<float*>(p);
   }
   *out = g_scratch_ptr[dev];
@@ -463,7 +470,7 @@ int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, c
   const Buf outs[3] = {{dq, z.g, 16}, {dk, z.g, 16}, {dv, z.g, 16}};
   if ((st = check_bufs(ins, 7, outs, 3))) return st;
   float* ws = nullptr;
-  if ((st = scratch_on_current_device(&ws))) return st;
+  if ((st = scratch_for_stream(static_cast<hipStream_t>(stream), &ws))) return st;
   const fa::BwdArgs a = bwd_args(q, k, v, o, lse, dout, dq, dk, dv, N, scale, blockmask, ws);
   return run_bwd(a, B * H, d, causal, blockmask != nullptr, kPre | kDkdv | kDq, stream);
 }

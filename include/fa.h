@@ -115,9 +115,12 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
  * FA_ERR_SCRATCH before any HIP call).  The call allocates and frees nothing.
  * Every call on one GPU shares that array: calls on one GPU that overlap in
  * time (different streams, or host threads without ordering) race on it and
- * must be serialised by the caller.  Other arguments, results and errors as
- * for fa_bwd; the first call on a device also queries the array's address
- * (FA_ERR_LAUNCH if the runtime refuses).
+ * must be serialised by the caller.  The array used is that of the GPU that
+ * runs `stream` (the current GPU for the default stream, NULL).  Other
+ * arguments, results and errors as for fa_bwd; the first call on a GPU also
+ * queries the array's address there, with that GPU made current for the
+ * query and the caller's current GPU restored (FA_ERR_LAUNCH if the runtime
+ * refuses).
  */
 int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
                    const float* lse, const void* dout, float* dq, float* dk, float* dv,

@@ -64,3 +64,29 @@ def test_noalloc_block_mask_and_binding():
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+def test_noalloc_on_a_side_stream():
+    """A non-default stream: the array is taken from the stream's GPU."""
+    import exact_io_aware_18_amd as fa
+
+    dev = device()
+    B, H, N, d = 1, 4, 777, 128
+    q, k, v, do = (t.to(dev) for t in make_qkvdo(B, H, N, d, "bf16", seed=75))
+    scale = default_scale(d)
+    o, lse = fa.fwd(q, k, v, scale, True)
+    ref = fa.bwd(q, k, v, o, lse, do, scale, True)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream(device=dev)  # default priority
+    outs = [Guarded(q.shape, torch.float32, dev) for _ in range(3)]
+    torch.cuda.synchronize()
+    print(f"\n[noalloc side stream] B={B} H={H} N={N} d={d} stream={side.cuda_stream:#x}", flush=True)
+    st = fa.fa_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                           do.data_ptr(), outs[0].view.data_ptr(), outs[1].view.data_ptr(),
+                           outs[2].view.data_ptr(), B, H, N, d, scale, 1, None, side.cuda_stream)
+    assert st == 0, fa.fa_strerror(st)
+    side.synchronize()
+    torch.cuda.synchronize()
+    for name, g, r in zip(("dq", "dk", "dv"), outs, ref):
+        g.check(name)
+        assert torch.equal(g.view, r), f"{name}: fa_bwd_noalloc on a side stream differs from fa_bwd"
