@@ -6,8 +6,11 @@ sub-workload, fa_fwd, then the three backward stages (fa_bwd_preprocess,
 fa_bwd_dkdv, fa_bwd_dq).  The default workload is long-context causal
 attention, B=1, H=16, N=16384, with both head dimensions d=64 and d=128 (the
 sequence length at which the forward target of half the bf16 MFMA peak is
-set).  HIP events recorded between consecutive launches on the launch stream
-give each kernel's average duration over the timed region.
+set).  The timed steps replay one HIP graph holding a step's calls (the host's
+launch gaps then leave the step time; --no-graph launches them call by call);
+the same number of steps launched call by call, with HIP events recorded
+between consecutive launches on the launch stream, give each kernel's average
+duration.
 
 FLOP convention: 4*d per unmasked (query, key) pair for the forward and 10*d
 for the backward (its five products, including the recomputation of S);
@@ -402,6 +405,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long_causal_16k", choices=sorted(BENCH_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time the steps launched call by call instead of as HIP graph replays")
     ap.add_argument("--sweep", choices=["sparsity", "io", "decode"],
                     help="run a block-sparsity or IO sweep instead of the step (one JSON line per point)")
     ap.add_argument("--sweep-reps", type=int, default=10)
@@ -464,12 +469,12 @@ def main():
         sub["ws"] = torch.empty(fa.fa_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
         subs.append(sub)
 
-    stream = torch.cuda.current_stream()
     drop = args.dropout
     nk = 2 if drop > 0 else 4  # timed calls per sub-workload per step
     seed = 0x5EED0000DEADBEEF
 
     def step_dropout(events=None):
+        stream = torch.cuda.current_stream()  # the capture stream while a graph is captured
         for si, s in enumerate(subs):
             if events is not None:
                 events[si * nk].record(stream)
@@ -485,6 +490,7 @@ def main():
     def step(events=None):
         if drop > 0:
             return step_dropout(events)
+        stream = torch.cuda.current_stream()  # the capture stream while a graph is captured
         for si, s in enumerate(subs):
             base = si * nk
             if events is not None:
@@ -517,6 +523,26 @@ def main():
         step()
     torch.cuda.synchronize()
 
+    # One step's calls captured in a HIP graph (they allocate nothing, record
+    # no memset and never synchronise): replaying it takes the host's launch
+    # gaps out of the step, which matters for the small workloads.
+    graph, graph_note = None, "not used (--no-graph)"
+    if not args.no_graph:
+        try:
+            side = torch.cuda.Stream()  # default priority
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                step()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                step()
+            torch.cuda.synchronize()
+            graph_note = "captured"
+        except Exception as e:  # capture refused: the eager steps are the measurement
+            graph, graph_note = None, f"capture failed ({type(e).__name__}: {e}); eager steps timed"
+
     nev = len(subs) * nk + 1
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -526,7 +552,16 @@ def main():
             step(evs[i])
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
+        ms_per_step_eager = (t1 - t0) * 1e3 / args.steps
+        ms_per_step = ms_per_step_eager
+        if graph is not None:
+            torch.cuda.synchronize()
+            t2 = time.perf_counter()
+            for i in range(args.steps):
+                graph.replay()
+            torch.cuda.synchronize()
+            t3 = time.perf_counter()
+            ms_per_step = (t3 - t2) * 1e3 / args.steps
 
     # cold regime: the inputs are evicted from every cache before each step
     cold = []
@@ -602,6 +637,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_eager": round(ms_per_step_eager, 4),
+        "hip_graph": graph_note,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -621,8 +658,10 @@ def main():
                     for k_, v_ in kernels.items()},
         "roofline": roofline,
         "roofline_fwd": roofline_fwd,
-        "timing": "warm: back-to-back steps, per-kernel mean (ms) and p10/p50/p90 over the timed "
-                  "steps from HIP events on the launch stream; cold: median over cold_steps steps, "
+        "timing": "ms_per_step: the timed steps as replays of one HIP graph holding a step's "
+                  "calls (hip_graph), else launched call by call; ms_per_step_eager: the same number "
+                  "of steps launched call by call with HIP events between the kernels, which give "
+                  "the per-kernel mean (ms) and p10/p50/p90; cold: median over cold_steps steps, "
                   "each after writing %d MiB of scratch" % (COLD_FLUSH_BYTES >> 20),
         "sclk": clk.summary(),
     }

@@ -120,7 +120,8 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
  * arguments, results and errors as for fa_bwd; the first call on a GPU also
  * queries the array's address there, with that GPU made current for the
  * query and the caller's current GPU restored (FA_ERR_LAUNCH if the runtime
- * refuses).
+ * refuses).  Under HIP graph capture, make the first call on a GPU outside
+ * the capture, so that the query is not recorded.
  */
 int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
                    const float* lse, const void* dout, float* dq, float* dk, float* dv,
