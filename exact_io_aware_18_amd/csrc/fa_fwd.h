@@ -402,8 +402,9 @@ __global__ __launch_bounds__(256, FwdTile<D>::MIN_WG) void fwd_bf16_kernel(FwdAr
 //   round r, phase 1:  A: M(r)      B: V2(r-1)   C: V1(r-1)
 //   round r, phase 2:  A: V1(r)     B: M(r)      C: V2(r-1)
 //   round r, phase 3:  A: V2(r)     B: V1(r)     C: M(r)
-// Here barriers split the round into its three phases (without them the
-// round is ~1.6% longer).
+// One barrier inside the round (between phases 2 and 3) and the one at its
+// end hold the groups: with a barrier between phases 1 and 2 as well the
+// forward was ~3% slower, and with none inside the round ~1.6% slower.
 // Round r reads K(r) and V(r-1); K(r+1) and V(r) are copied meanwhile into
 // the buffers round r-1 finished with.  Direct-to-LDS copies queue for the
 // CU's address unit and a wave stalls while its copies issue, so issuing
@@ -636,7 +637,7 @@ __global__ __launch_bounds__(256 * G, 1) void fwd_pp_kernel(FwdArgs a) {
 
   // round r (r = 0 .. ntiles): K(r) in kb[r&1], V(r-1) in vb[(r-1)&1].
   // Each group runs its own loop (the phase order differs); all execute the
-  // same barriers per round (one with G = 2, three with G = 3), the last
+  // same barriers per round (one with G = 2, two with G = 3), the last
   // after waiting for the copies.
   // mphase runs its last argument between the PV and the score products.
   // copies: see the schedule above; TileCopy covers 256 threads, so a
@@ -680,7 +681,6 @@ __global__ __launch_bounds__(256 * G, 1) void fwd_pp_kernel(FwdArgs a) {
       rounds([&] __device__ (int r, const char* kcur, char* knext, const char* vprev, char* vcur) __attribute__((always_inline)) {
         copyk(r, knext);
         mphase(r, kcur, vprev, [&] __device__ () { copyv(r, vcur); });
-        __syncthreads();
         vstep1(r);
         __syncthreads();
         vstep2(r);
@@ -689,7 +689,6 @@ __global__ __launch_bounds__(256 * G, 1) void fwd_pp_kernel(FwdArgs a) {
     } else if (grp == 1) {
       rounds([&] __device__ (int r, const char* kcur, char* knext, const char* vprev, char* vcur) __attribute__((always_inline)) {
         vstep2(r - 1);
-        __syncthreads();
         mphase(r, kcur, vprev, nomid);
         __syncthreads();
         vstep1(r);
@@ -698,7 +697,6 @@ __global__ __launch_bounds__(256 * G, 1) void fwd_pp_kernel(FwdArgs a) {
     } else {
       rounds([&] __device__ (int r, const char* kcur, char* knext, const char* vprev, char* vcur) __attribute__((always_inline)) {
         vstep1(r - 1);
-        __syncthreads();
         vstep2(r - 1);
         __syncthreads();
         mphase(r, kcur, vprev, nomid);
