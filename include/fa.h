@@ -33,7 +33,10 @@
  *     calls on different streams are safe.  Inputs are only read; outputs
  *     are fully overwritten.
  *   - Asynchrony: work is enqueued on `stream` (a hipStream_t, NULL = the
- *     null stream) and the call returns without waiting.
+ *     null stream) and the call returns without waiting.  A call only
+ *     launches kernels on that stream: it allocates nothing, records no
+ *     memset or copy and never synchronises, so calls can be captured into
+ *     a HIP graph (stream capture) and replayed.
  *   - Errors: arguments are checked before any HIP call, so a bad call
  *     returns a negative fa_status and enqueues nothing.  A failed launch
  *     returns FA_ERR_LAUNCH.  Faults inside a kernel surface at the caller's
