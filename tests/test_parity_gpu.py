@@ -296,3 +296,20 @@ def test_pingpong_negative_scale(d):
     negative scale, forward and backward against the oracle."""
     q, k, v, do = make_qkvdo(2, 64, 1000, d, "bf16", seed=43)
     full_parity(q, k, v, do, -default_scale(d), True, None, "bf16")
+
+
+@pytest.mark.parametrize("d,causal,N", [(64, True, 3), (128, False, 70), (64, False, 200), (128, True, 255),
+                                        (128, True, 300)])
+def test_pingpong_short_rows(d, causal, N):
+    """The two-group kernel on very short rows: 512 heads (B*H = 2*256) so the
+    grid reaches the 512 workgroups that select it, and N from 3 to 300, so a
+    workgroup's loop has 1 to 5 key tiles and its query tile is ragged.  The
+    first rounds (K copied by the second group, V by the first) and the last
+    are then the whole loop.  Forward and backward against the oracle on every
+    element."""
+    import exact_io_aware_18_amd as fa
+
+    B, H = 2, 256
+    assert fa.fa_fwd_query_rows(B, H, N, d, int(causal), 0, 0) == 256, "expected the two-group kernel"
+    q, k, v, do = make_qkvdo(B, H, N, d, "bf16", seed=61)
+    full_parity(q, k, v, do, default_scale(d), causal, None, "bf16")
