@@ -259,6 +259,113 @@ __global__ __launch_bounds__(256, DkdvTile<D>::MIN_WG) void bwd_dkdv_kernel(BwdA
     }
   };
 
+  // The same tile with the two sub-blocks overlapped inside the wave, for
+  // tiles without masked entries and without dropout: the S and dP products
+  // of sub-block 1 go between the softmax steps of sub-block 0, and the dV
+  // and dK products of sub-block 0 between those of sub-block 1, so that
+  // the wave's own products run while it issues VALU work.  Every value is
+  // computed as in compute_seq and dK, dV sum the sub-blocks in the same
+  // order, so the results are the same bit for bit.
+  auto compute_pipe = [&] __device__ (const char* qt, const char* dt, const float* lt, const float* et) {
+    auto rowop = [&] __device__ (int sb, int m) -> bf16x8 {
+      return lds_read16(((m & 1) ? dt : qt) + 32 * sb * PITCH + toff.rows[m >> 1]);
+    };
+    auto trop = [&] __device__ (int sb, int m) -> bf16x8 {
+      return toff.read_tr(((m & 2) ? qt : dt) + 32 * sb * PITCH, m & 1, m >> 2);
+    };
+    constexpr int NM1 = 2 * NKC, NM2 = 4 * NCT;  // products per sub-block
+    f32x16 S[2], dP[2];
+    // sub-block 0: S and dP
+    {
+      bf16x8 ring[4];
+#pragma unroll
+      for (int m = 0; m < 3; ++m) ring[m] = rowop(0, m);
+      S[0] = f32x16{};
+      dP[0] = f32x16{};
+#pragma unroll
+      for (int m = 0; m < NM1; ++m) {
+        if (m + 3 < NM1) ring[(m + 3) & 3] = rowop(0, m + 3);
+        if (m & 1) dP[0] = mfma32(ring[m & 3], vf[m >> 1], dP[0]);
+        else S[0] = mfma32(ring[m & 3], kf[m >> 1], S[0]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // softmax step of sub-block sb, elements 4u .. 4u+3 (group u of lse and
+    // D), straight into the bf16 P and dS operands (k-step u / 2)
+    bf16x8 pb[2][2], sbv[2][2];
+    auto soft4 = [&] __device__ (int sb, int u, const f32x4& l4, const f32x4& e4) __attribute__((always_inline)) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * u + e;
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[sb][r], c, -l4[e]));
+        pb[sb][u >> 1][r & 7] = (__bf16)pv;
+        sbv[sb][u >> 1][r & 7] = (__bf16)(pv * (dP[sb][r] - e4[e]));
+      }
+    };
+    auto lvec = [&] __device__ (const float* v, int sb, int u) -> f32x4 {
+      return *reinterpret_cast<const f32x4*>(v + 32 * sb + 16 * (u >> 1) + 8 * h + 4 * (u & 1));
+    };
+    // sub-block 1's S and dP products between sub-block 0's softmax steps
+    {
+      f32x4 l4 = lvec(lt, 0, 0), e4 = lvec(et, 0, 0);  // one group ahead
+      bf16x8 ring[3];  // two products ahead: the softmax steps cover the reads
+#pragma unroll
+      for (int m = 0; m < 2; ++m) ring[m] = rowop(1, m);
+      S[1] = f32x16{};
+      dP[1] = f32x16{};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+#pragma unroll
+        for (int j = 0; j < NM1 / 4; ++j) {
+          const int m = (NM1 / 4) * u + j;
+          if (m + 2 < NM1) ring[(m + 2) % 3] = rowop(1, m + 2);
+          if (m & 1) dP[1] = mfma32(ring[m % 3], vf[m >> 1], dP[1]);
+          else S[1] = mfma32(ring[m % 3], kf[m >> 1], S[1]);
+        }
+        const f32x4 lc = l4, ec = e4;
+        if (u + 1 < 4) { l4 = lvec(lt, 0, u + 1); e4 = lvec(et, 0, u + 1); }
+        soft4(0, u, lc, ec);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // sub-block 0's dV and dK products between sub-block 1's softmax steps
+    {
+      f32x4 l4 = lvec(lt, 1, 0), e4 = lvec(et, 1, 0);
+      bf16x8 ring[3];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) ring[m] = trop(0, m);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+#pragma unroll
+        for (int j = 0; j < NM2 / 4; ++j) {
+          const int m = (NM2 / 4) * u + j;
+          if (m + 2 < NM2) ring[(m + 2) % 3] = trop(0, m + 2);
+          const int ct = m >> 2;
+          if (m & 2) dk[ct] = mfma32(ring[m % 3], sbv[0][m & 1], dk[ct]);
+          else dv[ct] = mfma32(ring[m % 3], pb[0][m & 1], dv[ct]);
+        }
+        const f32x4 lc = l4, ec = e4;
+        if (u + 1 < 4) { l4 = lvec(lt, 1, u + 1); e4 = lvec(et, 1, u + 1); }
+        soft4(1, u, lc, ec);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // sub-block 1's dV and dK products
+    {
+      bf16x8 ring[4];
+#pragma unroll
+      for (int m = 0; m < 3; ++m) ring[m] = trop(1, m);
+#pragma unroll
+      for (int m = 0; m < NM2; ++m) {
+        if (m + 3 < NM2) ring[(m + 3) & 3] = trop(1, m + 3);
+        const int ct = m >> 2;
+        if (m & 2) dk[ct] = mfma32(ring[m & 3], sbv[1][m & 1], dk[ct]);
+        else dv[ct] = mfma32(ring[m & 3], pb[1][m & 1], dv[ct]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
   const int kb = k0 >> 7;  // mask column (BK == 128)
   const int nqt_all = (N + BQ - 1) / BQ;
   const int qb_lo = CAUSAL ? kb : 0;
@@ -294,7 +401,12 @@ __global__ __launch_bounds__(256, DkdvTile<D>::MIN_WG) void bwd_dkdv_kernel(BwdA
         nv = load_vec(q1);
       }
       const int q0 = tile_of(t) * BQ;
-      if (kw0 < N) compute_seq(qc, dc, lc, ec, q0);
+      // no masked entry in the tile: every query follows every key, all in range
+      const bool plain = !DROP && BQ == 64 && !(CAUSAL && q0 < kw0 + 31) && q0 + BQ <= N;
+      if (kw0 < N) {
+        if (plain) compute_pipe(qc, dc, lc, ec);
+        else compute_seq(qc, dc, lc, ec, q0);
+      }
       if (t + 1 < ntiles) store_vec(ln, en, nv);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
