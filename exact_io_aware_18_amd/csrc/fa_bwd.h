@@ -259,14 +259,18 @@ __global__ __launch_bounds__(256, DkdvTile<D>::MIN_WG) void bwd_dkdv_kernel(BwdA
     }
   };
 
-  // The same tile with the two sub-blocks overlapped inside the wave, for
-  // tiles without masked entries and without dropout: the S and dP products
-  // of sub-block 1 go between the softmax steps of sub-block 0, and the dV
-  // and dK products of sub-block 0 between those of sub-block 1, so that
-  // the wave's own products run while it issues VALU work.  Every value is
-  // computed as in compute_seq and dK, dV sum the sub-blocks in the same
-  // order, so the results are the same bit for bit.
-  auto compute_pipe = [&] __device__ (const char* qt, const char* dt, const float* lt, const float* et) {
+  // Without dropout, the two sub-blocks overlapped inside the wave: the S and
+  // dP products of sub-block 1 go between the softmax steps of sub-block 0,
+  // and the dV and dK products of sub-block 0 between those of sub-block 1,
+  // so that the wave's own products run while it issues VALU work.  Every
+  // value is computed as in compute_seq and dK, dV sum the sub-blocks in the
+  // same order.  A sub-block whose queries all precede the wave's keys, which
+  // compute_seq skips, is computed here with P = dS = 0: its products add
+  // exact zeros to accumulators that are never -0, so the results are the
+  // same bit for bit.  One path for every tile also keeps the accumulators in
+  // the same registers from tile to tile.
+  static_assert(BQ == 64, "the overlapped tile has two 32-query sub-blocks");
+  auto compute_pipe = [&] __device__ (const char* qt, const char* dt, const float* lt, const float* et, int q0) {
     auto rowop = [&] __device__ (int sb, int m) -> bf16x8 {
       return lds_read16(((m & 1) ? dt : qt) + 32 * sb * PITCH + toff.rows[m >> 1]);
     };
@@ -291,15 +295,31 @@ __global__ __launch_bounds__(256, DkdvTile<D>::MIN_WG) void bwd_dkdv_kernel(BwdA
       }
     }
     // softmax step of sub-block sb, elements 4u .. 4u+3 (group u of lse and
-    // D), straight into the bf16 P and dS operands (k-step u / 2)
+    // D), straight into the bf16 P and dS operands (k-step u / 2); causal and
+    // range masks only on the tiles that need them
+    bool edge[2];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      const int qs0 = q0 + 32 * sb;
+      edge[sb] = (CAUSAL && qs0 < kw0 + 31) || (qs0 + 32 > N);
+    }
     bf16x8 pb[2][2], sbv[2][2];
     auto soft4 = [&] __device__ (int sb, int u, const f32x4& l4, const f32x4& e4) __attribute__((always_inline)) {
+      float pv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[sb][4 * u + e], c, -l4[e]));
+      if (edge[sb]) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int qq = q0 + 32 * sb + acc_row(4 * u + e, h);
+          if ((CAUSAL && kj > qq) || qq >= N) pv[e] = 0.f;
+        }
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * u + e;
-        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[sb][r], c, -l4[e]));
-        pb[sb][u >> 1][r & 7] = (__bf16)pv;
-        sbv[sb][u >> 1][r & 7] = (__bf16)(pv * (dP[sb][r] - e4[e]));
+        pb[sb][u >> 1][r & 7] = (__bf16)pv[e];
+        sbv[sb][u >> 1][r & 7] = (__bf16)(pv[e] * (dP[sb][r] - e4[e]));
       }
     };
     auto lvec = [&] __device__ (const float* v, int sb, int u) -> f32x4 {
@@ -401,11 +421,9 @@ __global__ __launch_bounds__(256, DkdvTile<D>::MIN_WG) void bwd_dkdv_kernel(BwdA
         nv = load_vec(q1);
       }
       const int q0 = tile_of(t) * BQ;
-      // no masked entry in the tile: every query follows every key, all in range
-      const bool plain = !DROP && BQ == 64 && !(CAUSAL && q0 < kw0 + 31) && q0 + BQ <= N;
       if (kw0 < N) {
-        if (plain) compute_pipe(qc, dc, lc, ec);
-        else compute_seq(qc, dc, lc, ec, q0);
+        if constexpr (DROP) compute_seq(qc, dc, lc, ec, q0);
+        else compute_pipe(qc, dc, lc, ec, q0);
       }
       if (t + 1 < ntiles) store_vec(ln, en, nv);
       __builtin_amdgcn_s_waitcnt(0);
@@ -893,13 +911,14 @@ __global__ __launch_bounds__(256, DqTile<D>::MIN_WG) void bwd_dq_kernel(BwdArgs 
     }
   };
 
-  // The same tile with its two 32-key halves overlapped inside the wave, for
-  // d = 64 tiles without masked entries, causal mask or dropout: half 1's S
-  // and dP products go between half 0's exp and dS steps, the dQ products
-  // over half 0's keys between half 1's, and those over half 1's keys last.
-  // Each dQ accumulator still sums the tile's k-steps in order and every
-  // value is computed as in compute, so the results are the same bit for bit.
-  auto compute_pipe = [&] __device__ (const char* kt, const char* vt) {
+  // At d = 64 without dropout, the tile's two 32-key halves overlapped inside
+  // the wave: half 1's S and dP products go between half 0's exp and dS
+  // steps, the dQ products over half 0's keys between half 1's, and those
+  // over half 1's keys last.  Each dQ accumulator still sums the tile's
+  // k-steps in order and every value is computed as in compute, so the
+  // results are the same bit for bit.  It serves every tile, masked ones
+  // included, so that the accumulators stay in the same registers.
+  auto compute_pipe = [&] __device__ (const char* kt, const char* vt, int k0) {
     constexpr int NM1 = 2 * NKC;
     auto rowop = [&] __device__ (int t2, int m) -> bf16x8 {
       return lds_read16(((m & 1) ? vt : kt) + toff.rows[m >> 1] + 32 * t2 * PITCH);
@@ -920,13 +939,29 @@ __global__ __launch_bounds__(256, DqTile<D>::MIN_WG) void bwd_dq_kernel(BwdArgs 
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // exp and dS of half t2, rows 4u .. 4u+3, straight into its bf16 operands
+    // exp and dS of half t2, rows 4u .. 4u+3, straight into its bf16
+    // operands; causal and range masks only on the halves that need them
+    bool edge[2];
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const int ks0 = k0 + 32 * t2;
+      edge[t2] = (CAUSAL && ks0 + 31 > qw0) || (ks0 + 32 > N);
+    }
     auto soft4 = [&] __device__ (int t2, int u) __attribute__((always_inline)) {
+      float pv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[t2][4 * u + e], c, -lse2));
+      if (edge[t2]) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = k0 + 32 * t2 + acc_row(4 * u + e, h);
+          if ((CAUSAL && key > qi) || key >= N) pv[e] = 0.f;
+        }
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * u + e;
-        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[t2][r], c, -lse2));
-        dsb[2 * t2 + (r >> 3)][r & 7] = (__bf16)(pv * (dP[t2][r] - Di));
+        dsb[2 * t2 + (r >> 3)][r & 7] = (__bf16)(pv[e] * (dP[t2][r] - Di));
       }
     };
     // half 1's S and dP between half 0's steps
@@ -1013,11 +1048,8 @@ __global__ __launch_bounds__(256, DqTile<D>::MIN_WG) void bwd_dq_kernel(BwdArgs 
         cp.issue(vn, Vh, k1, N, w);
       }
       const int k0 = tile_of(t) * BC;
-      // no masked entry in the tile (all keys in range), no causal mask: with
-      // causal masking the overlapped tile measured flat to 9% slower
-      const bool plain = !DROP && !CAUSAL && D == 64 && k0 + BC <= N;
       if (active(k0)) {
-        if (plain) compute_pipe(kc_, vc_);
+        if constexpr (!DROP && D == 64) compute_pipe(kc_, vc_, k0);
         else compute(kc_, vc_, k0);
       }
       __builtin_amdgcn_s_waitcnt(0);
