@@ -244,8 +244,13 @@ __global__ __launch_bounds__(256, FwdTile<D>::MIN_WG) void fwd_bf16_kernel(FwdAr
         n1 = mfma32(ka1[kc], qf[kc], n1);
       }
     }
-    // ---- ... while P runs on the VALU (discarded below when noref)
-    float lt = make_p(noref ? 0.f : Mref);
+    // ---- ... while P runs on the VALU (discarded below when noref).  The
+    // reference is opaque to the compiler: otherwise it specialises P for
+    // noref into a second block, and the products and the exponentials can
+    // no longer share one scheduling region.
+    float mb = noref ? 0.f : Mref;
+    asm volatile("" : "+v"(mb));
+    float lt = make_p(mb);
     if constexpr (T::PIPE) {
       // interleave: K reads three k-steps ahead, one MFMA per ~7 VALU ops
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 1);
@@ -260,8 +265,10 @@ __global__ __launch_bounds__(256, FwdTile<D>::MIN_WG) void fwd_bf16_kernel(FwdAr
     }
     __builtin_amdgcn_sched_barrier(0);
     // ---- rare: row max over the tile (v_max3 chains, both halves), lazy
-    // move of the reference with the rescale of O and l, P again
-    if (noref || wave_any(!(lt <= kSkipSum))) {
+    // move of the reference with the rescale of O and l, P again.  One
+    // ballot over both conditions, so that P above is computed on every path
+    // and stays in the scheduling region of the products.
+    if (wave_any(Mref == -INFINITY || !(lt <= kSkipSum))) {
       float m0 = fmaxf(s0[0], s0[1]), m1 = fmaxf(s1[0], s1[1]);
 #pragma unroll
       for (int r = 2; r < 16; r += 2) {
