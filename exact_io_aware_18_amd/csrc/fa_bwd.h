@@ -175,100 +175,17 @@ __global__ __launch_bounds__(256, DkdvTile<D>::MIN_WG) void bwd_dkdv_kernel(BwdA
     }
   };
 
-  // The tile's two 32-query sub-blocks, one after the other.
-  auto compute_seq = [&] __device__ (const char* qt, const char* dt, const float* lt, const float* et, int q0) {
-#pragma unroll
-    for (int sb = 0; sb < BQ / 32; ++sb) {
-      const int qs0 = q0 + 32 * sb;
-      if (CAUSAL && qs0 + 31 < kw0) continue;  // every query precedes every key
-      const char* qs = qt + 32 * sb * PITCH;
-      const char* ds = dt + 32 * sb * PITCH;
-      // S = Q K^T and dP = dO V^T: MFMA m takes Q (m even) or dO (m odd)
-      // rows of k-step m/2, read three MFMAs ahead into a ring of four, one
-      // scheduling step per MFMA, so each wait covers exactly its operand
-      auto rowop = [&] __device__ (int m) -> bf16x8 { return lds_read16(((m & 1) ? ds : qs) + toff.rows[m >> 1]); };
-      f32x16 S = f32x16{}, dP = f32x16{};
-      {
-        bf16x8 ring[4];
-#pragma unroll
-        for (int m = 0; m < 3; ++m) ring[m] = rowop(m);
-#pragma unroll
-        for (int m = 0; m < 2 * NKC; ++m) {
-          if (m + 3 < 2 * NKC) ring[(m + 3) & 3] = rowop(m + 3);
-          if (m & 1) dP = mfma32(ring[m & 3], vf[m >> 1], dP);
-          else S = mfma32(ring[m & 3], kf[m >> 1], S);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-      // lane's queries: 32sb + 16*hf + 8h + e, e = 0..7
-      const bool edge = (CAUSAL && qs0 < kw0 + 31) || (qs0 + 32 > N);
-      float p[16], dsv[16];
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const f32x4 l0 = *reinterpret_cast<const f32x4*>(lt + 32 * sb + 16 * hf + 8 * h);
-        const f32x4 l1 = *reinterpret_cast<const f32x4*>(lt + 32 * sb + 16 * hf + 8 * h + 4);
-        const f32x4 e0 = *reinterpret_cast<const f32x4*>(et + 32 * sb + 16 * hf + 8 * h);
-        const f32x4 e1 = *reinterpret_cast<const f32x4*>(et + 32 * sb + 16 * hf + 8 * h + 4);
-        uint32_t kbits = 0xFFu;
-        if constexpr (DROP) {
-          const int i0 = qs0 + 16 * hf + 8 * h;
-          kbits = keep4_keylane(a.drop, bh, i0, kj, lane) | (keep4_keylane(a.drop, bh, i0 + 4, kj, lane) << 4);
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int r = 8 * hf + e;
-          const float lv = e < 4 ? l0[e] : l1[e - 4];
-          const float dvv = e < 4 ? e0[e] : e1[e - 4];
-          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], c, -lv));
-          if (edge) {
-            const int qq = qs0 + acc_row(r, h);
-            if ((CAUSAL && kj > qq) || qq >= N) pv = 0.f;
-          }
-          if constexpr (DROP) {
-            const bool kept = (kbits >> e) & 1u;
-            p[r] = kept ? pv : 0.f;
-            dsv[r] = pv * ((kept ? dP[r] * a.drop.keep_scale : 0.f) - dvv);
-          } else {
-            p[r] = pv;
-            dsv[r] = pv * (dP[r] - dvv);
-          }
-        }
-      }
-      const bf16x8 pb0 = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-      const bf16x8 pb1 = to_bf16x8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
-      const bf16x8 sb0 = to_bf16x8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
-      const bf16x8 sb1 = to_bf16x8(dsv[8], dsv[9], dsv[10], dsv[11], dsv[12], dsv[13], dsv[14], dsv[15]);
-      __builtin_amdgcn_sched_barrier(0);
-      // dV^T += dO^T P and dK^T += Q^T dS (scale applied at the end): MFMA
-      // m = 4 ct + j, j = dV k-step 0, 1, dK k-step 0, 1; transposed
-      // operands in a ring as above
-      auto trop = [&] __device__ (int m) -> bf16x8 { return toff.read_tr((m & 2) ? qs : ds, m & 1, m >> 2); };
-      {
-        bf16x8 ring[4];
-#pragma unroll
-        for (int m = 0; m < 3; ++m) ring[m] = trop(m);
-#pragma unroll
-        for (int m = 0; m < 4 * NCT; ++m) {
-          if (m + 3 < 4 * NCT) ring[(m + 3) & 3] = trop(m + 3);
-          const int ct = m >> 2;
-          if (m & 2) dk[ct] = mfma32(ring[m & 3], (m & 1) ? sb1 : sb0, dk[ct]);
-          else dv[ct] = mfma32(ring[m & 3], (m & 1) ? pb1 : pb0, dv[ct]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-    }
-  };
-
-  // Without dropout, the two sub-blocks overlapped inside the wave: the S and
-  // dP products of sub-block 1 go between the softmax steps of sub-block 0,
-  // and the dV and dK products of sub-block 0 between those of sub-block 1,
-  // so that the wave's own products run while it issues VALU work.  Every
-  // value is computed as in compute_seq and dK, dV sum the sub-blocks in the
-  // same order.  A sub-block whose queries all precede the wave's keys, which
-  // compute_seq skips, is computed here with P = dS = 0: its products add
-  // exact zeros to accumulators that are never -0, so the results are the
-  // same bit for bit.  One path for every tile also keeps the accumulators in
-  // the same registers from tile to tile.
+  // One 64-query tile: two 32-query sub-blocks, overlapped inside the wave.
+  // The S and dP products of sub-block 1 go between the softmax steps of
+  // sub-block 0 (four elements each), and the dV and dK products of
+  // sub-block 0 between those of sub-block 1, so that the wave's own products
+  // run while it issues VALU work; dK and dV sum sub-block 0, then 1.  Causal
+  // and range masks apply per element, behind a uniform branch per
+  // sub-block; with dropout each step of four queries makes the one generator
+  // call that covers them.  A sub-block whose queries all precede the wave's
+  // keys is not skipped: with P = dS = 0 its products add exact zeros to
+  // accumulators that are never -0.  One path for every tile keeps the
+  // accumulators in the same registers from tile to tile.
   static_assert(BQ == 64, "the overlapped tile has two 32-query sub-blocks");
   auto compute_pipe = [&] __device__ (const char* qt, const char* dt, const float* lt, const float* et, int q0) {
     auto rowop = [&] __device__ (int sb, int m) -> bf16x8 {
@@ -315,11 +232,20 @@ __global__ __launch_bounds__(256, DkdvTile<D>::MIN_WG) void bwd_dkdv_kernel(BwdA
           if ((CAUSAL && kj > qq) || qq >= N) pv[e] = 0.f;
         }
       }
+      uint32_t kbits = 0xFu;  // keep bits of queries q0 + 32 sb + 16 (u / 2) + 8h + 4 (u % 2) + e
+      if constexpr (DROP)
+        kbits = keep4_keylane(a.drop, bh, q0 + 32 * sb + 16 * (u >> 1) + 8 * h + 4 * (u & 1), kj, lane);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * u + e;
-        pb[sb][u >> 1][r & 7] = (__bf16)pv[e];
-        sbv[sb][u >> 1][r & 7] = (__bf16)(pv[e] * (dP[sb][r] - e4[e]));
+        if constexpr (DROP) {
+          const bool kept = (kbits >> e) & 1u;
+          pb[sb][u >> 1][r & 7] = (__bf16)(kept ? pv[e] : 0.f);
+          sbv[sb][u >> 1][r & 7] = (__bf16)(pv[e] * ((kept ? dP[sb][r] * a.drop.keep_scale : 0.f) - e4[e]));
+        } else {
+          pb[sb][u >> 1][r & 7] = (__bf16)pv[e];
+          sbv[sb][u >> 1][r & 7] = (__bf16)(pv[e] * (dP[sb][r] - e4[e]));
+        }
       }
     };
     auto lvec = [&] __device__ (const float* v, int sb, int u) -> f32x4 {
@@ -421,10 +347,7 @@ __global__ __launch_bounds__(256, DkdvTile<D>::MIN_WG) void bwd_dkdv_kernel(BwdA
         nv = load_vec(q1);
       }
       const int q0 = tile_of(t) * BQ;
-      if (kw0 < N) {
-        if constexpr (DROP) compute_seq(qc, dc, lc, ec, q0);
-        else compute_pipe(qc, dc, lc, ec, q0);
-      }
+      if (kw0 < N) compute_pipe(qc, dc, lc, ec, q0);
       if (t + 1 < ntiles) store_vec(ln, en, nv);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
@@ -911,13 +834,14 @@ __global__ __launch_bounds__(256, DqTile<D>::MIN_WG) void bwd_dq_kernel(BwdArgs 
     }
   };
 
-  // At d = 64 without dropout, the tile's two 32-key halves overlapped inside
-  // the wave: half 1's S and dP products go between half 0's exp and dS
-  // steps, the dQ products over half 0's keys between half 1's, and those
-  // over half 1's keys last.  Each dQ accumulator still sums the tile's
-  // k-steps in order and every value is computed as in compute, so the
-  // results are the same bit for bit.  It serves every tile, masked ones
-  // included, so that the accumulators stay in the same registers.
+  // At d = 64, the tile's two 32-key halves overlapped inside the wave: half
+  // 1's S and dP products go between half 0's exp and dS steps, the dQ
+  // products over half 0's keys between half 1's, and those over half 1's
+  // keys last.  Each dQ accumulator still sums the tile's k-steps in order
+  // and every value is computed as in compute (with dropout, each step of
+  // four keys makes the one generator call that covers them), so the results
+  // are the same bit for bit.  It serves every tile, masked ones included, so
+  // that the accumulators stay in the same registers.
   auto compute_pipe = [&] __device__ (const char* kt, const char* vt, int k0) {
     constexpr int NM1 = 2 * NKC;
     auto rowop = [&] __device__ (int t2, int m) -> bf16x8 {
@@ -958,10 +882,19 @@ __global__ __launch_bounds__(256, DqTile<D>::MIN_WG) void bwd_dq_kernel(BwdArgs 
           if ((CAUSAL && key > qi) || key >= N) pv[e] = 0.f;
         }
       }
+      uint32_t kbits = 0xFu;  // keep bits of the four keys k0 + 32 t2 + acc_row(4u + e, h)
+      if constexpr (DROP) kbits = keep4(a.drop, bh, qi, k0 + 32 * t2 + 16 * (u >> 1) + 8 * h + 4 * (u & 1));
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * u + e;
-        dsb[2 * t2 + (r >> 3)][r & 7] = (__bf16)(pv[e] * (dP[t2][r] - Di));
+        float dsv;
+        if constexpr (DROP) {
+          const bool kept = (kbits >> e) & 1u;
+          dsv = pv[e] * ((kept ? dP[t2][r] * a.drop.keep_scale : 0.f) - Di);
+        } else {
+          dsv = pv[e] * (dP[t2][r] - Di);
+        }
+        dsb[2 * t2 + (r >> 3)][r & 7] = (__bf16)dsv;
       }
     };
     // half 1's S and dP between half 0's steps
@@ -1049,7 +982,7 @@ __global__ __launch_bounds__(256, DqTile<D>::MIN_WG) void bwd_dq_kernel(BwdArgs 
       }
       const int k0 = tile_of(t) * BC;
       if (active(k0)) {
-        if constexpr (!DROP && D == 64) compute_pipe(kc_, vc_, k0);
+        if constexpr (D == 64) compute_pipe(kc_, vc_, k0);
         else compute(kc_, vc_, k0);
       }
       __builtin_amdgcn_s_waitcnt(0);
